@@ -1,0 +1,91 @@
+"""Rounding to the storage and quantisation formats, from their definitions.
+
+Test infrastructure only (see the package docstring).
+
+* bfloat16: the upper 16 bits of an IEEE-754 binary32, rounded to nearest,
+  ties to even, on the 16 discarded bits.
+* binary16: IEEE-754 half precision; numpy's float16 cast is a correctly
+  rounded (ties-to-even) conversion and serves as the library primitive.
+* e4m3fn (OCP 8-bit floating point, E4M3 flavour): 1 sign, 4 exponent bits
+  with bias 7, 3 mantissa bits; no infinities, S.1111.111 is NaN, largest
+  finite value 448 = 1.75 * 2**8, smallest normal 2**-6, subnormals
+  m * 2**-9 for m = 1..7.  Conversion rounds to nearest even; values beyond
+  448 in magnitude saturate to 448 (the saturating conversion the variant
+  needs, since its inputs are bounded by 448 by construction).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even; NaN stays NaN."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (b >> 16) & 1
+    r = ((b + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    if nan.any():
+        r = np.where(nan, ((b >> 16) | 0x40).astype(np.uint16), r)
+    return r
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Value of x after rounding to bf16, as float64 (exact)."""
+    return bf16_bits_to_f64(f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
+
+
+def round_f16(x) -> np.ndarray:
+    """Value of x after rounding to IEEE binary16, as float64 (exact)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)
+
+
+# ---- e4m3fn ---------------------------------------------------------------
+
+E4M3_MAX = 448.0
+_E4M3_BIAS = 7
+
+
+def e4m3_bits_to_f64(bits) -> np.ndarray:
+    """Decode e4m3fn bit patterns (uint8) to float64."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    s = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 0x7
+    normal = s * (1.0 + m / 8.0) * np.exp2(e - _E4M3_BIAS)
+    sub = s * (m / 8.0) * np.exp2(1 - _E4M3_BIAS)
+    v = np.where(e == 0, sub, normal)
+    return np.where((e == 0xF) & (m == 0x7), np.nan, v)
+
+
+# All 127 non-negative finite e4m3 magnitudes in increasing order (code = index).
+_E4M3_POS = e4m3_bits_to_f64(np.arange(0, 0x7F, dtype=np.uint8))
+
+
+def f64_to_e4m3_bits(x) -> np.ndarray:
+    """Round to the nearest e4m3fn value (ties to the even code), saturating at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    sat = a >= E4M3_MAX
+    a_c = np.minimum(a, E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a_c, side="left")          # first value >= a
+    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    vhi, vlo = _E4M3_POS[hi], _E4M3_POS[lo]
+    dhi, dlo = vhi - a_c, a_c - vlo
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(vhi == a_c, hi, code)
+    code = np.where(sat, 0x7E, code).astype(np.uint8)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    out = code | sign
+    return np.where(np.isnan(x), np.uint8(0x7F), out).astype(np.uint8)
+
+
+def round_e4m3(x) -> np.ndarray:
+    """Value of x after rounding to e4m3fn (saturating), as float64."""
+    return e4m3_bits_to_f64(f64_to_e4m3_bits(x))

@@ -1,0 +1,139 @@
+"""Exact emulation of the INT8-QK / FP8-PV attention variant (SageAttention style).
+
+Test infrastructure only (see the package docstring).
+
+Source: handbook page "算子加速：注意力、编译与融合", section "SageAttention":
+K is smoothed by subtracting a mean (removing its outlier channels), Q and K
+are quantised to INT8 so that Q K^T runs on integer matrix cores, and P and V
+go through FP8 with wide accumulation.  The pages print no quantised result,
+so the numerical choices below are this project's readings, applied the same
+way on both sides:
+
+  * K smoothing: kmean[b,h,:] = mean of K over all N tokens, summed in float64
+    and rounded once to float32; Ks = fp32(K - kmean).  Softmax ignores a
+    per-row constant, and q . kmean is one, so O is unchanged by smoothing.
+  * INT8 Q and Ks: one scale per (b, h, block of 64 tokens from token 0; the
+    last block may be partial) over all D channels: a = max |X|,
+    inv = fp32(127 / a), x8 = clamp(rint(fp32(X * inv)), -127, 127),
+    s = fp32(a / 127); an all-zero block gives x8 = 0, s = 0.
+  * FP8 V: one scale per (b, h, channel): av = max_t |V|,
+    v8 = e4m3(fp32(V * fp32(448 / av))), sv = fp32(av / 448).
+  * Scores s = (sum_d q8 k8) * sq * sk * scale (the integer dot product is
+    exact), then the mask as in the unquantised formula.
+  * P is quantised against the running max of the blocked recurrence: for the
+    key tiles of ``kv_block`` keys in ascending order, m_j = max(m_{j-1},
+    tile max), P = exp(s - m_j) <= 1, l = l * exp(m_{j-1} - m_j) + sum P (the
+    unquantised P), acc = acc * exp(m_{j-1} - m_j) + sum_t e4m3(448 P_t) v8_t.
+  * O = acc * sv / (448 l); a row with every key masked gives O = 0.
+
+The score, exp and accumulation steps run in float64; the quantisers use the
+float32 steps written above, reproduced with numpy float32 (IEEE, correctly
+rounded per operation).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .rounding import round_e4m3
+
+QBLOCK = 64          # tokens per INT8 scale block
+E4M3_MAX = 448.0
+
+
+def k_mean(k_head) -> np.ndarray:
+    """Token mean of one head's K [N, D], rounded once to float32."""
+    k = np.asarray(k_head, dtype=np.float64)
+    return (k.sum(axis=0) / k.shape[0]).astype(np.float32)
+
+
+def quantise_int8_blocks(x_head, block=QBLOCK):
+    """x_head [N, D] (float32 values) -> (x8 int8 [N, D], scale float32 [ceil(N/block)])."""
+    x = np.asarray(x_head, dtype=np.float32)
+    n = x.shape[0]
+    nb = -(-n // block)
+    x8 = np.zeros(x.shape, dtype=np.int8)
+    sc = np.zeros(nb, dtype=np.float32)
+    for g in range(nb):
+        xb = x[g * block:(g + 1) * block]
+        a = np.float32(np.abs(xb).max()) if xb.size else np.float32(0)
+        if a == 0:
+            continue
+        inv = np.float32(np.float32(127.0) / a)
+        y = (xb * inv).astype(np.float32)
+        x8[g * block:(g + 1) * block] = np.clip(np.rint(y), -127, 127).astype(np.int8)
+        sc[g] = np.float32(a / np.float32(127.0))
+    return x8, sc
+
+
+def quantise_fp8_channels(v_head):
+    """v_head [N, D] -> (v8 e4m3 values as float64 [N, D], per-channel scale float32 [D])."""
+    v = np.asarray(v_head, dtype=np.float32)
+    av = np.abs(v).max(axis=0).astype(np.float32)
+    safe = np.where(av == 0, np.float32(1), av).astype(np.float32)
+    mul = np.where(av == 0, np.float32(0), (np.float32(E4M3_MAX) / safe).astype(np.float32)).astype(np.float32)
+    y = (v * mul[None, :]).astype(np.float32)
+    v8 = round_e4m3(y.astype(np.float64))
+    sv = np.where(av == 0, np.float32(0), (av / np.float32(E4M3_MAX)).astype(np.float32)).astype(np.float32)
+    return v8, sv
+
+
+def quantise_head(q_head, k_head, v_head):
+    """All quantised operands of one (b, h) head."""
+    km = k_mean(k_head)
+    ks = (np.asarray(k_head, dtype=np.float32) - km[None, :]).astype(np.float32)
+    q8, sq = quantise_int8_blocks(q_head)
+    k8, sk = quantise_int8_blocks(ks)
+    v8, sv = quantise_fp8_channels(v_head)
+    return dict(kmean=km, ks=ks, q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv)
+
+
+def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quantise_p=True):
+    """Blocked recurrence over key tiles with P quantised against the running max."""
+    row_ids = np.asarray(row_ids, dtype=np.int64)
+    q8 = qz["q8"][row_ids].astype(np.float64)
+    k8 = qz["k8"].astype(np.float64)
+    n = k8.shape[0]
+    s = q8 @ k8.T                                           # exact integers
+    s = s * qz["sq"][row_ids // QBLOCK].astype(np.float64)[:, None]
+    s = s * qz["sk"][np.arange(n) // QBLOCK].astype(np.float64)[None, :]
+    s = s * float(scale)
+    if key_len is not None:
+        s[:, int(key_len):] = -np.inf
+    R = len(row_ids)
+    D = qz["v8"].shape[1]
+    m = np.full((R, 1), -np.inf)
+    l = np.zeros((R, 1))
+    acc = np.zeros((R, D))
+    for j in range(0, n, kv_block):
+        st = s[:, j:j + kv_block]
+        m_new = np.maximum(m, st.max(axis=1, keepdims=True))
+        ref = np.where(np.isfinite(m_new), m_new, 0.0)
+        p = np.exp(st - ref)
+        alpha = np.exp(m - ref)
+        l = l * alpha + p.sum(axis=1, keepdims=True)
+        p8 = round_e4m3(p * E4M3_MAX) if quantise_p else p * E4M3_MAX
+        acc = acc * alpha + p8 @ qz["v8"][j:j + kv_block]
+        m = m_new
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o = acc * qz["sv"].astype(np.float64)[None, :] / (E4M3_MAX * l)
+    return np.where(l == 0, 0.0, o)
+
+
+def emulate_rows(q_head, k_head, v_head, row_ids, scale, kv_block, key_len=None, qz=None):
+    """Quantised-variant output for selected query rows of one head (float64, before
+    the output rounding)."""
+    if qz is None:
+        qz = quantise_head(q_head, k_head, v_head)
+    return _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len)
+
+
+def emulate(q, k, v, scale, kv_block, key_len=None):
+    """Full [B, H, N, D] emulation (small shapes)."""
+    q = np.asarray(q)
+    B, H, N, D = q.shape
+    out = np.zeros((B, H, N, np.asarray(v).shape[3]))
+    for b in range(B):
+        for h in range(H):
+            kl = None if key_len is None else int(np.asarray(key_len)[b])
+            out[b, h] = emulate_rows(q[b, h], k[b, h], v[b, h], np.arange(N), scale, kv_block, kl)
+    return out

@@ -1,0 +1,211 @@
+"""MI355X (gfx950) attention forward: Python binding of libfa.so.
+
+The C ABI is declared in include/fa.h.  This module only marshals arguments:
+the raw entry points ``fa_fwd`` / ``fa_fwd_int8qk`` / ... take the same
+arguments as their C counterparts (device pointers as ints), and the tensor
+wrappers ``fwd`` / ``fwd_int8qk`` take torch tensors that already live on the
+GPU, allocate the outputs with torch and pass torch's current stream.  Every
+step of the computation runs in the HIP kernels; there is no fallback: if
+libfa.so is missing or cannot be loaded, calls raise ``FAUnavailable``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_MASK_NONE, FA_MASK_ADDITIVE, FA_MASK_KEYLEN = 0, 1, 2
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
+FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
+
+EXPORTED = ("fa_fwd", "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk", "fa_int8qk_kv_block",
+            "fa_status_string", "fa_last_hip_error", "fa_abi_version")
+
+
+class FAUnavailable(RuntimeError):
+    """libfa.so is not built or cannot be loaded."""
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = f"{where} failed: {status} ({status_string(status)})"
+        if status == FA_ERR_HIP:
+            msg += f": {last_hip_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+class fa_mask_t(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("ptr", ctypes.c_void_p),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_q", ctypes.c_int64), ("stride_k", ctypes.c_int64)]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so once and declare the C signatures."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise FAUnavailable(f"{LIB_PATH} is not built; run attention_fa_fwd_04_amd.build")
+    try:
+        h = ctypes.CDLL(LIB_PATH)
+    except OSError as e:
+        raise FAUnavailable(f"cannot load {LIB_PATH}: {e}") from e
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    mp = ctypes.POINTER(fa_mask_t)
+    h.fa_fwd.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp]
+    h.fa_fwd.restype = i32
+    h.fa_fwd_int8qk_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    h.fa_fwd_int8qk_workspace_bytes.restype = sz
+    h.fa_fwd_int8qk.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    h.fa_fwd_int8qk.restype = i32
+    h.fa_int8qk_kv_block.argtypes = []
+    h.fa_int8qk_kv_block.restype = i32
+    h.fa_status_string.argtypes = [i32]
+    h.fa_status_string.restype = ctypes.c_char_p
+    h.fa_last_hip_error.argtypes = []
+    h.fa_last_hip_error.restype = ctypes.c_char_p
+    h.fa_abi_version.argtypes = []
+    h.fa_abi_version.restype = i32
+    _lib_handle = h
+    return h
+
+
+# ---- raw entry points (same names and arguments as the C ABI) -------------
+
+def fa_fwd(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream) -> int:
+    return lib().fa_fwd(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream)
+
+
+def fa_fwd_int8qk_workspace_bytes(B, H, N, D) -> int:
+    return lib().fa_fwd_int8qk_workspace_bytes(B, H, N, D)
+
+
+def fa_fwd_int8qk(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace,
+                  workspace_bytes, hip_stream) -> int:
+    return lib().fa_fwd_int8qk(q, k, v, o, lse, mask, B, H, N, D, scale, dtype,
+                               workspace, workspace_bytes, hip_stream)
+
+
+def fa_int8qk_kv_block() -> int:
+    return lib().fa_int8qk_kv_block()
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(status).decode()
+
+
+def fa_last_hip_error() -> str:
+    return lib().fa_last_hip_error().decode()
+
+
+def fa_abi_version() -> int:
+    return lib().fa_abi_version()
+
+
+status_string = fa_status_string
+last_hip_error = fa_last_hip_error
+
+
+# ---- torch tensor wrappers ------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, D], got {tuple(t.shape)}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, D]")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v dtypes differ")
+
+
+def _mask_struct(q, attn_mask, key_len, keep):
+    """Build fa_mask_t from a torch mask.  Boolean masks follow the convention
+    that False / 0 drops a key and become additive 0 / -inf float32."""
+    import torch
+    B, H, N, _ = q.shape
+    if attn_mask is not None and key_len is not None:
+        raise ValueError("give either attn_mask or key_len, not both")
+    if key_len is not None:
+        kl = key_len.to(device=q.device, dtype=torch.int32).contiguous()
+        if kl.shape != (B,):
+            raise ValueError(f"key_len must have shape [{B}]")
+        keep.append(kl)
+        return fa_mask_t(FA_MASK_KEYLEN, kl.data_ptr(), 0, 0, 0, 0)
+    if attn_mask is not None:
+        m = attn_mask
+        if m.dtype == torch.bool:
+            m = torch.zeros(m.shape, dtype=torch.float32, device=m.device).masked_fill_(~m, float("-inf"))
+        m = m.to(device=q.device, dtype=torch.float32)
+        while m.dim() < 4:
+            m = m.unsqueeze(0)
+        m = m.expand(B, H, N, N)
+        strides = [s if sz > 1 else 0 for s, sz in zip(m.stride(), m.shape)]
+        keep.append(m)
+        return fa_mask_t(FA_MASK_ADDITIVE, m.data_ptr(), *strides)
+    return None
+
+
+def fwd(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
+        return_lse: bool = False, out=None):
+    """O = softmax(scale * q k^T + mask) v for GPU tensors [B, H, N, D]."""
+    import torch
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    keep = []
+    m = _mask_struct(q, attn_mask, key_len, keep)
+    st = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                lse.data_ptr() if lse is not None else None,
+                ctypes.byref(m) if m is not None else None,
+                B, H, N, D, scale, _dtype_code(q), st)
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd")
+    return (o, lse) if return_lse else o
+
+
+def fwd_int8qk(q, k, v, *, key_len=None, scale: Optional[float] = None,
+               return_lse: bool = False, workspace=None, out=None):
+    """The INT8-QK / FP8-PV variant for GPU tensors [B, H, N, 128] (bf16 / fp16)."""
+    import torch
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    need = fa_fwd_int8qk_workspace_bytes(B, H, N, D)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
+    keep = []
+    m = _mask_struct(q, None, key_len, keep)
+    st = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_fwd_int8qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       lse.data_ptr() if lse is not None else None,
+                       ctypes.byref(m) if m is not None else None,
+                       B, H, N, D, scale, _dtype_code(q), ws.data_ptr(), ws.numel(), st)
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd_int8qk")
+    return (o, lse) if return_lse else o

@@ -1,0 +1,184 @@
+// C ABI of libfa.so: host-side validation, kernel selection and launch.
+// Declarations and conventions: include/fa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_fwd_kernel.hpp"
+#include "fa_int8qk.hpp"
+
+namespace {
+
+thread_local char g_hip_err[256] = "";
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("FA_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+const char* dtype_name(int dt) {
+  switch (dt) {
+    case FA_F32: return "f32";
+    case FA_F16: return "f16";
+    case FA_BF16: return "bf16";
+    default: return "?";
+  }
+}
+
+int record_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    std::snprintf(g_hip_err, sizeof(g_hip_err), "%s: %s", what, hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+// Arguments common to both entry points.
+int check_common(const void* q, const void* k, const void* v, void* o, const float* lse,
+                 const fa_mask_t* mask, int B, int H, int N, int D, float scale) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return FA_ERR_SHAPE;
+  const int64_t nqt = (N + 127) / 128;
+  if ((int64_t)B * H * nqt > INT32_MAX) return FA_ERR_SHAPE;
+  if ((int64_t)B * H * (int64_t)N > (int64_t)1 << 40) return FA_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return FA_ERR_ALIGN;
+  if (mask) {
+    if (mask->kind != FA_MASK_NONE && mask->kind != FA_MASK_ADDITIVE && mask->kind != FA_MASK_KEYLEN)
+      return FA_ERR_ARG;
+    if (mask->kind != FA_MASK_NONE) {
+      if (!mask->ptr) return FA_ERR_NULL;
+      if (!aligned(mask->ptr, 4)) return FA_ERR_ALIGN;
+    }
+    if (mask->kind == FA_MASK_ADDITIVE &&
+        (mask->stride_b < 0 || mask->stride_h < 0 || mask->stride_q < 0 || mask->stride_k < 0))
+      return FA_ERR_ARG;
+  }
+  return FA_OK;
+}
+
+template <typename T, int D, int MASK>
+int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
+               int B, int H, int N, float scale, hipStream_t st) {
+  constexpr int BC = (sizeof(T) == 4) ? 32 : 64;
+  using C = fa::FwdCfg<T, D, BC, MASK>;
+  const int nqt = (N + C::BR - 1) / C::BR;
+  const int grid = B * H * nqt;
+  if (log_enabled())
+    std::fprintf(stderr, "[fa] fa_fwd dtype=%s D=%d mask=%d B=%d H=%d N=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
+                 sizeof(T) == 4 ? "f32" : "f16/bf16", D, MASK, B, H, N, grid, C::NT, C::BR, BC, 2 * C::BUF);
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, BC, MASK>), dim3(grid), dim3(C::NT), 0, st,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                     static_cast<T*>(o), lse, m, H, N, nqt, scale * fa::kLog2e);
+  return record_launch("fa_fwd_kernel");
+}
+
+template <typename T, int D>
+int dispatch_mask(int kind, const void* q, const void* k, const void* v, void* o, float* lse,
+                  fa::MaskArgs m, int B, int H, int N, float scale, hipStream_t st) {
+  switch (kind) {
+    case FA_MASK_NONE: return launch_fwd<T, D, fa::kMaskNone>(q, k, v, o, lse, m, B, H, N, scale, st);
+    case FA_MASK_ADDITIVE: return launch_fwd<T, D, fa::kMaskAdd>(q, k, v, o, lse, m, B, H, N, scale, st);
+    case FA_MASK_KEYLEN: return launch_fwd<T, D, fa::kMaskLen>(q, k, v, o, lse, m, B, H, N, scale, st);
+    default: return FA_ERR_ARG;
+  }
+}
+
+template <typename T>
+int dispatch_d(int D, int kind, const void* q, const void* k, const void* v, void* o, float* lse,
+               fa::MaskArgs m, int B, int H, int N, float scale, hipStream_t st) {
+  switch (D) {
+    case 32: return dispatch_mask<T, 32>(kind, q, k, v, o, lse, m, B, H, N, scale, st);
+    case 40: return dispatch_mask<T, 40>(kind, q, k, v, o, lse, m, B, H, N, scale, st);
+    case 128: return dispatch_mask<T, 128>(kind, q, k, v, o, lse, m, B, H, N, scale, st);
+    default: return FA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+           fa_dtype_t dtype, void* hip_stream) {
+  int rc = check_common(q, k, v, o, lse, mask, B, H, N, D, scale);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (D != 32 && D != 40 && D != 128) return FA_ERR_UNSUPPORTED;
+  const int kind = mask ? mask->kind : FA_MASK_NONE;
+  fa::MaskArgs m{nullptr, 0, 0, 0, 0};
+  if (kind != FA_MASK_NONE) m = fa::MaskArgs{mask->ptr, mask->stride_b, mask->stride_h, mask->stride_q, mask->stride_k};
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  switch (dtype) {
+    case FA_F32: return dispatch_d<float>(D, kind, q, k, v, o, lse, m, B, H, N, scale, st);
+    case FA_F16: return dispatch_d<_Float16>(D, kind, q, k, v, o, lse, m, B, H, N, scale, st);
+    case FA_BF16: return dispatch_d<__bf16>(D, kind, q, k, v, o, lse, m, B, H, N, scale, st);
+    default: return FA_ERR_UNSUPPORTED;
+  }
+}
+
+FA_API size_t fa_fwd_int8qk_workspace_bytes(int B, int H, int N, int D) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return 0;
+  return fa::int8qk_workspace_layout(B, H, N, D).total;
+}
+
+FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                  fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                  void* hip_stream) {
+  int rc = check_common(q, k, v, o, lse, mask, B, H, N, D, scale);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (D != 128) return FA_ERR_UNSUPPORTED;
+  const int kind = mask ? mask->kind : FA_MASK_NONE;
+  if (kind == FA_MASK_ADDITIVE) return FA_ERR_UNSUPPORTED;
+  const fa::Int8Layout lay = fa::int8qk_workspace_layout(B, H, N, D);
+  if (!workspace) return FA_ERR_WORKSPACE;
+  if (workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
+  const int* key_len = (kind == FA_MASK_KEYLEN) ? static_cast<const int*>(mask->ptr) : nullptr;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (log_enabled())
+    std::fprintf(stderr, "[fa] fa_fwd_int8qk dtype=%s D=%d keylen=%d B=%d H=%d N=%d ws=%zu\n",
+                 dtype_name(dtype), D, key_len != nullptr, B, H, N, lay.total);
+  if (dtype == FA_BF16)
+    rc = fa::launch_int8qk<__bf16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+  else
+    rc = fa::launch_int8qk<_Float16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+  if (rc != FA_OK) return rc;
+  return record_launch("fa_fwd_int8qk");
+}
+
+FA_API int fa_int8qk_kv_block(void) { return fa::kInt8Bc; }
+
+FA_API const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H, N or D not positive, or the problem is too large";
+    case FA_ERR_UNSUPPORTED: return "dtype / head dimension / mask combination not supported";
+    case FA_ERR_ALIGN: return "a pointer is not aligned as required";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_ARG: return "invalid argument";
+    case FA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+FA_API const char* fa_last_hip_error(void) { return g_hip_err; }
+
+FA_API int fa_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Shared device helpers for the gfx950 attention kernels: vector types, MFMA
+// wrappers over 16-byte operand chunks, conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float    f32x2  __attribute__((ext_vector_type(2)));
+typedef float    f32x4  __attribute__((ext_vector_type(4)));
+typedef float    f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t  i32x4  __attribute__((ext_vector_type(4)));
+typedef int32_t  i32x8  __attribute__((ext_vector_type(8)));
+typedef int32_t  i32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2  __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4  __attribute__((ext_vector_type(4)));
+typedef __bf16   bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16   bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2  __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8  __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum MaskKind { kMaskNone = 0, kMaskAdd = 1, kMaskLen = 2 };
+
+struct MaskArgs {
+  const void* ptr;
+  int64_t sb, sh, sq, sk;
+};
+
+template <typename T> struct Elt;
+template <> struct Elt<float>    { static constexpr int kBytes = 4; };
+template <> struct Elt<_Float16> { static constexpr int kBytes = 2; };
+template <> struct Elt<__bf16>   { static constexpr int kBytes = 2; };
+
+// 32x32 MFMA accumulate over one 16-byte operand chunk per lane.  For the
+// 16-bit types that is one 32x32x16 instruction (8 elements per lane); for
+// float it is four 32x32x2 instructions, element e of each lane's chunk
+// feeding instruction e.  A and B always take the same element of the same
+// lane half, so any consistent assignment of the contraction index to
+// (lane half, element) gives the same sum.
+template <typename T> __device__ __forceinline__ f32x16 mfma_chunk(u32x4 a, u32x4 b, f32x16 c);
+
+template <> __device__ __forceinline__ f32x16 mfma_chunk<__bf16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mfma_chunk<_Float16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mfma_chunk<float>(u32x4 a, u32x4 b, f32x16 c) {
+  // Bit-cast whole vectors, then index: a bit-cast of a single ext-vector
+  // element is not reliably lowered to that element.
+  const f32x4 af = __builtin_bit_cast(f32x4, a);
+  const f32x4 bf = __builtin_bit_cast(f32x4, b);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(af.x, bf.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(af.y, bf.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(af.z, bf.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(af.w, bf.w, c, 0, 0, 0);
+  return c;
+}
+
+// Two floats -> two 16-bit values in one dword (round to nearest even).
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// 16 bytes of operand from 16/sizeof(T) consecutive floats.
+template <typename T> __device__ __forceinline__ u32x4 pack_chunk(const float* p) {
+  u32x4 r;
+  r.x = pack2<T>(p[0], p[1]);
+  r.y = pack2<T>(p[2], p[3]);
+  r.z = pack2<T>(p[4], p[5]);
+  r.w = pack2<T>(p[6], p[7]);
+  return r;
+}
+template <> __device__ __forceinline__ u32x4 pack_chunk<float>(const float* p) {
+  const f32x4 v = {p[0], p[1], p[2], p[3]};
+  return __builtin_bit_cast(u32x4, v);
+}
+
+// Four consecutive outputs.
+template <typename T> __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {
+  u32x2 r = {pack2<T>(a, b), pack2<T>(c, d)};
+  *reinterpret_cast<u32x2*>(dst) = r;
+}
+template <> __device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
+  f32x4 r = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(dst) = r;
+}
+
+// Logical tile for a workgroup.  Consecutive workgroup ids are dealt round
+// robin to the 8 XCDs; this remap hands each XCD one contiguous run of
+// logical tiles, so the query tiles of a head (which re-read the same K/V)
+// run on the same XCD and share its L2.  Bijective for any grid size.
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+  const int xcd = bid & 7, k = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + k;
+}
+
+__device__ __forceinline__ float wave_max_halves(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+}  // namespace fa

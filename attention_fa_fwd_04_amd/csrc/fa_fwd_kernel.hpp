@@ -1,0 +1,334 @@
+// Attention forward kernel for gfx950 (fp32 / fp16 / bf16).
+//
+// Method: handbook page "算子加速：注意力、编译与融合", section
+// "注意力：从 O(N²) 显存到分块" (figure and blocked code): for each query tile,
+// stream K/V tiles through on-chip memory, form the score tile, update the
+// running row max m and denominator l, rescale the accumulator by
+// exp(m_old - m_new) and add P V; only O (and the row log-sum-exp) is written.
+//
+// Work split.  A workgroup is 4 waves and owns 128 consecutive query rows of
+// one (b, h) head; wave w owns rows 32w..32w+31.  Each wave computes the
+// transposed score tile S^T = K Q^T with 32x32 MFMAs (keys on the M side,
+// queries on the N side), so lane (n, h) = (lane % 32, lane / 32) holds query
+// n and, per 32-key block, the 16 keys 8g + 4h + r (g, r in 0..3) in
+// accumulator register 4g + r.  The softmax is then lane-local: a row max
+// needs one exchange with the other lane half, the row sum is kept per lane
+// half and added once at the end.
+//
+// The output is accumulated transposed too, O^T += V^T P^T, so the running
+// rescale by alpha = exp2(m_old - m_new) touches only the lane's own query.
+// The P^T operand is the lane's own scores (no data movement); the V^T
+// operand needs, per lane, consecutive keys at a fixed channel, so the V tile
+// is transposed on its way into LDS and its key order permuted within each
+// 32-key block (key 8g + 4h + r stored at position 16h + 4g + r), which makes
+// each lane's 16 keys contiguous and 16-byte readable.
+//
+// Memory path.  K rows go to LDS as-is (row stride padded by 16 bytes, which
+// keeps the 16-lane phases of ds_read_b128 on distinct banks); V goes through
+// registers, is transposed with byte permutes and written as V^T.  The next
+// K/V tile is fetched into registers while the current one is consumed, and
+// written to the other half of a double buffer afterwards: one barrier per
+// tile.  Q stays in registers in MFMA operand layout for the whole loop.
+//
+// Exponentials are exp2 with scale*log2(e) folded into the FMA that subtracts
+// the running max.  Key tails (N % 64) and key-length masks drop keys on the
+// boundary tile only; tiles wholly past the key length are never visited.
+#pragma once
+
+#include "fa_common.hpp"
+
+namespace fa {
+
+template <typename T, int D, int BC, int MASK>
+struct FwdCfg {
+  static constexpr int E = Elt<T>::kBytes;
+  static constexpr int EPC = 16 / E;              // elements per 16-byte chunk
+  static constexpr int DCH = D * E / 16;          // chunks per row
+  static constexpr int QKS = (DCH + 1) / 2;       // MFMA steps over D (2 chunks each)
+  static constexpr int KSTR = 32 * QKS + 16;      // K row stride in LDS, bytes
+  static constexpr int PVB = (D + 31) / 32;       // 32-channel blocks of O^T
+  static constexpr int VSTR = BC * E + 16;        // V^T row stride in LDS, bytes
+  static constexpr int KBYTES = BC * KSTR;
+  static constexpr int VBYTES = 32 * PVB * VSTR;
+  static constexpr int BUF = KBYTES + VBYTES;
+  static constexpr int SB = BC / 32;              // 32-key blocks per tile
+  static constexpr int NT = 256;                  // threads per workgroup
+  static constexpr int BR = 128;                  // query rows per workgroup
+  static constexpr int KITEMS = BC * DCH;
+  static constexpr int KIT = (KITEMS + NT - 1) / NT;
+  static constexpr int VITEMS = (BC / 4) * DCH;
+  static constexpr int VIT = (VITEMS + NT - 1) / NT;
+  static_assert(D * E % 16 == 0, "rows must be whole 16-byte chunks");
+  static_assert(BC % 32 == 0, "key tile must be whole 32-key blocks");
+  static_assert(2 * BUF <= 160 * 1024, "double buffer must fit in LDS");
+};
+
+template <typename T, int D, int BC, int MASK>
+__global__ __launch_bounds__(256) void fa_fwd_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    T* __restrict__ O, float* __restrict__ LSE, MaskArgs mask,
+    int H, int N, int nqt, float c_log2) {
+  using C = FwdCfg<T, D, BC, MASK>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 31, lh = lane >> 5;
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / nqt, qt = logical - bh * nqt;
+  const int b = bh / H, h = bh - b * H;
+  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const uint8_t* Qh = reinterpret_cast<const uint8_t*>(Q + head_off);
+  const uint8_t* Kh = reinterpret_cast<const uint8_t*>(K + head_off);
+  const uint8_t* Vh = reinterpret_cast<const uint8_t*>(V + head_off);
+
+  int n_eff = N;
+  if constexpr (MASK == kMaskLen) {
+    const int L = reinterpret_cast<const int*>(mask.ptr)[b];
+    n_eff = L < 0 ? 0 : (L > N ? N : L);
+  }
+  const int ntiles = (n_eff + BC - 1) / BC;
+
+  const int q_row = qt * C::BR + wave * 32 + ln;
+  const bool q_ok = q_row < N;
+
+  // Q in B-operand layout: step s, lane half h holds chunk 2s + h of its row.
+  u32x4 qreg[C::QKS];
+#pragma unroll
+  for (int s = 0; s < C::QKS; ++s) {
+    const int ch = 2 * s + lh;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (q_ok && ch < C::DCH)
+      z = *reinterpret_cast<const u32x4*>(Qh + (size_t)q_row * (D * C::E) + ch * 16);
+    qreg[s] = z;
+  }
+
+  // Zero the padding the tile writes never touch: K chunks past D (QK steps
+  // are 2 chunks wide) and V^T rows past D (PV blocks are 32 channels).
+  if constexpr (2 * C::QKS > C::DCH) {
+    for (int r = tid; r < 2 * BC; r += C::NT) {
+      uint8_t* p = smem + (r / BC) * C::BUF + (r % BC) * C::KSTR + C::DCH * 16;
+      for (int c = 0; c < (2 * C::QKS - C::DCH) * 16; c += 16)
+        *reinterpret_cast<u32x4*>(p + c) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  if constexpr (32 * C::PVB > D) {
+    constexpr int rows = 32 * C::PVB - D;
+    constexpr int chunks = BC * C::E / 16;
+    for (int it = tid; it < 2 * rows * chunks; it += C::NT) {
+      const int buf = it / (rows * chunks), rem = it % (rows * chunks);
+      uint8_t* p = smem + buf * C::BUF + C::KBYTES + (D + rem / chunks) * C::VSTR + (rem % chunks) * 16;
+      *reinterpret_cast<u32x4*>(p) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // ---- tile staging (global -> registers -> LDS) ----
+  u32x4 kst[C::KIT];
+  u32x4 vst[C::VIT][4];
+
+  auto load_tile = [&](int j) {
+    const int kv0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < C::KIT; ++i) {
+      const int it = tid + i * C::NT;
+      const int row = it / C::DCH;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (it < C::KITEMS && kv0 + row < n_eff)
+        z = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv0 * (D * C::E) + (size_t)it * 16);
+      kst[i] = z;
+    }
+#pragma unroll
+    for (int i = 0; i < C::VIT; ++i) {
+      const int it = tid + i * C::NT;
+      const int kg = it % (BC / 4), dc = it / (BC / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kv0 + 4 * kg + r;
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if (it < C::VITEMS && key < n_eff)
+          z = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * (D * C::E) + dc * 16);
+        vst[i][r] = z;
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    uint8_t* kb = smem + buf * C::BUF;
+    uint8_t* vb = kb + C::KBYTES;
+#pragma unroll
+    for (int i = 0; i < C::KIT; ++i) {
+      const int it = tid + i * C::NT;
+      if (it < C::KITEMS) {
+        const int row = it / C::DCH, c = it - row * C::DCH;
+        *reinterpret_cast<u32x4*>(kb + row * C::KSTR + c * 16) = kst[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::VIT; ++i) {
+      const int it = tid + i * C::NT;
+      if (it >= C::VITEMS) continue;
+      const int kg = it % (BC / 4), dc = it / (BC / 4);
+      const int key = 4 * kg;                       // first of 4 consecutive keys
+      const int kk = key & 31;
+      const int pos = (key & ~31) + 16 * ((kk >> 2) & 1) + 4 * (kk >> 3);
+      uint8_t* base = vb + pos * C::E;
+      if constexpr (C::E == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u32x4 w = {vst[i][0][e], vst[i][1][e], vst[i][2][e], vst[i][3][e]};
+          *reinterpret_cast<u32x4*>(base + (dc * 4 + e) * C::VSTR) = w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          u32x2 w;
+          w.x = __builtin_amdgcn_perm(vst[i][1][e >> 1], vst[i][0][e >> 1], sel);
+          w.y = __builtin_amdgcn_perm(vst[i][3][e >> 1], vst[i][2][e >> 1], sel);
+          *reinterpret_cast<u32x2*>(base + (dc * 8 + e) * C::VSTR) = w;
+        }
+      }
+    }
+  };
+
+  float m_run = -INFINITY;   // running max, log2 units
+  float l_run = 0.f;         // this lane half's share of the denominator
+  f32x16 acc[C::PVB];
+#pragma unroll
+  for (int p = 0; p < C::PVB; ++p)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[p][i] = 0.f;
+
+  // Additive masks are scaled to log2 units before the max; otherwise the
+  // scale is folded into the exp2 argument.
+  constexpr bool kPre = (MASK == kMaskAdd);
+  const float cs = kPre ? 1.f : c_log2;
+  const float* mrow = nullptr;
+  if constexpr (kPre) {
+    mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh +
+           (int64_t)(q_ok ? q_row : 0) * mask.sq;
+  }
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);
+    const uint8_t* kb = smem + buf * C::BUF;
+    const uint8_t* vb = kb + C::KBYTES;
+    const int kv0 = j * BC;
+
+    // S^T = K Q^T
+    f32x16 s[C::SB];
+#pragma unroll
+    for (int G = 0; G < C::SB; ++G) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[G][i] = 0.f;
+#pragma unroll
+      for (int st = 0; st < C::QKS; ++st) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * G + ln) * C::KSTR + (2 * st + lh) * 16);
+        s[G] = mfma_chunk<T>(a, qreg[st], s[G]);
+      }
+    }
+
+    // mask, row max
+    if constexpr (kPre) {
+#pragma unroll
+      for (int G = 0; G < C::SB; ++G)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
+          float t = -INFINITY;
+          if (key < N) {
+            const float mv = q_ok ? mrow[(int64_t)key * mask.sk] : 0.f;
+            t = __builtin_fmaf(s[G][i], c_log2, mv * kLog2e);
+          }
+          s[G][i] = t;
+        }
+    } else if (kv0 + BC > n_eff) {
+#pragma unroll
+      for (int G = 0; G < C::SB; ++G)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
+          if (key >= n_eff) s[G][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int G = 0; G < C::SB; ++G)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[G][i]);
+    mx = wave_max_halves(mx);
+    const float m_new = fmaxf(m_run, mx * cs);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+
+    // P = exp2(S*c - m), row sum
+    float psum = 0.f;
+#pragma unroll
+    for (int G = 0; G < C::SB; ++G)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[G][i], cs, -m_use));
+        s[G][i] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+
+    // rescale the accumulator only when some row's max moved
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int p = 0; p < C::PVB; ++p)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[p][i] *= alpha;
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int G = 0; G < C::SB; ++G) {
+#pragma unroll
+      for (int cc = 0; cc < 16 / C::EPC; ++cc) {
+        float pv[C::EPC];
+#pragma unroll
+        for (int e = 0; e < C::EPC; ++e) pv[e] = s[G][cc * C::EPC + e];
+        const u32x4 bop = pack_chunk<T>(pv);
+#pragma unroll
+        for (int p = 0; p < C::PVB; ++p) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(
+              vb + (32 * p + ln) * C::VSTR + (32 * G + 16 * lh + cc * C::EPC) * C::E);
+          acc[p] = mfma_chunk<T>(a, bop, acc[p]);
+        }
+      }
+    }
+
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, lse = ln 2 * (m + log2 l) ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_ok) {
+    T* orow = O + head_off + (size_t)q_row * D;
+#pragma unroll
+    for (int p = 0; p < C::PVB; ++p)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * p + 8 * g + 4 * lh;
+        if (d0 < D)
+          store4<T>(orow + d0, acc[p][4 * g] * inv, acc[p][4 * g + 1] * inv,
+                    acc[p][4 * g + 2] * inv, acc[p][4 * g + 3] * inv);
+      }
+    if (LSE != nullptr && lh == 0)
+      LSE[(size_t)bh * N + q_row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace fa

@@ -114,19 +114,28 @@ def head(w: Workload, tid: int, b: int, h: int) -> torch.Tensor:
     return torch.from_numpy(head_f32(w, tid, b, h)).to(w.torch_dtype)
 
 
-def make_inputs(w: Workload) -> dict:
-    """CPU tensors q, k, v [B, H, N, D] in the storage dtype (+ key_len)."""
+def make_inputs(w: Workload, threads: int = 8) -> dict:
+    """CPU tensors q, k, v [B, H, N, D] in the storage dtype (+ key_len).
+
+    Heads are drawn on a thread pool (numpy's generators release the GIL);
+    the per-head streams make the result independent of the thread count."""
+    from concurrent.futures import ThreadPoolExecutor
     if w.wid == 1 and (w.B, w.H, w.N, w.D) == (1, 4, 256, 32):
         torch.manual_seed(0)
         q, k, v = (torch.randn(w.B, w.H, w.N, w.D) for _ in range(3))
         return {"q": q, "k": k, "v": v, "key_len": None}
     out = {}
     for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V)):
-        t = torch.empty((w.B, w.H, w.N, w.D), dtype=w.torch_dtype)
-        for b in range(w.B):
-            for h in range(w.H):
-                t[b, h] = head(w, tid, b, h)
-        out[name] = t
+        x = np.empty((w.B, w.H, w.N, w.D), dtype=np.float32)
+
+        def fill(bh, x=x, tid=tid):
+            b, h = divmod(bh, w.H)
+            x[b, h] = head_f32(w, tid, b, h)
+
+        with ThreadPoolExecutor(max(1, threads)) as ex:
+            list(ex.map(fill, range(w.B * w.H)))
+        out[name] = torch.from_numpy(x).to(w.torch_dtype)
+        del x
     kl = key_lengths(w)
     out["key_len"] = None if kl is None else torch.from_numpy(kl)
     return out

@@ -1,0 +1,131 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) attention-forward library libfa.so.
+ *
+ * The operation (handbook page "算子加速：注意力、编译与融合", section
+ * "注意力：从 O(N²) 显存到分块", and the case-study page, section 3.1):
+ *
+ *     O[b,h,i,:] = sum_j softmax_j( scale * Q[b,h,i,:] . K[b,h,j,:] + M[b,h,i,j] ) V[b,h,j,:]
+ *
+ * computed tile by tile with a running row max and denominator so the N x N
+ * score matrix never reaches device memory.  Non-causal; no dropout; forward
+ * only.  The mask M is added after scaling (case-study page, section 2.3) and
+ * is either an additive float32 array or a per-batch valid key count.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors q, k, v, o are contiguous [B, H, N, D] with D fastest
+ *     (essay page, sections 2.1 and 5.3, case-study page, section 3.3), in
+ *     the element type `dtype`; o has the same type as the inputs.
+ *   - All pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates or frees memory and never synchronises; work is queued on
+ *     `hip_stream` (a hipStream_t; NULL means the null stream) and the call
+ *     returns as soon as it is queued.
+ *   - q, k, v, o and workspace must be 16-byte aligned; lse and mask 4-byte.
+ *   - Arguments are validated on the host before anything is queued; on an
+ *     error nothing is launched and a negative FA_ERR_* code is returned.
+ *   - A row whose every key is masked yields O = 0 and lse = -inf.
+ *   - Output is bitwise deterministic for identical inputs and launch
+ *     configuration (fixed reduction order, no atomics).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define FA_API __attribute__((visibility("default")))
+#else
+#define FA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype_t;
+
+typedef enum {
+  FA_MASK_NONE = 0,
+  /* float32 values added to the scaled scores; -inf drops a key.  Element
+   * (b,h,i,j) is read at ptr[b*stride_b + h*stride_h + i*stride_q + j*stride_k];
+   * a stride of 0 broadcasts that dimension. */
+  FA_MASK_ADDITIVE = 1,
+  /* int32 len[B] on the device: keys j >= len[b] are dropped for every query
+   * of batch entry b (padding of dynamically batched requests, case-study
+   * page, section 2.2).  Values outside [0, N] are clamped to it. */
+  FA_MASK_KEYLEN = 2
+} fa_mask_kind_t;
+
+typedef struct {
+  int32_t kind;       /* fa_mask_kind_t */
+  const void* ptr;    /* device pointer, see fa_mask_kind_t */
+  int64_t stride_b, stride_h, stride_q, stride_k;   /* FA_MASK_ADDITIVE only, in elements */
+} fa_mask_t;
+
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,       /* B, H, N or D not positive, or the problem is too large */
+  FA_ERR_UNSUPPORTED = -3, /* dtype / D / mask combination not built */
+  FA_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
+  FA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+  FA_ERR_ARG = -6,         /* any other invalid argument (scale, mask kind, ...) */
+  FA_ERR_HIP = -7          /* the HIP runtime rejected a launch; see fa_last_hip_error */
+};
+
+/*
+ * Attention forward.
+ *   q, k, v  [B,H,N,D] dtype (read)         o   [B,H,N,D] dtype (written)
+ *   lse      [B,H,N] float32 or NULL: natural-log log-sum-exp of each row's
+ *            scaled, masked scores (essay page, section 3.1: the kernel also
+ *            emits the row log-sum-exp), -inf for a fully masked row.
+ *   mask     NULL or a descriptor (FA_MASK_NONE is the same as NULL).
+ *   scale    multiplies Q.K; must be finite and > 0 (1/sqrt(D) is usual).
+ * Supported: dtype F32, F16, BF16; D in {32, 40, 128}; any N >= 1.
+ */
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+           fa_dtype_t dtype, void* hip_stream);
+
+/*
+ * INT8-QK / FP8-PV variant (handbook page, section "SageAttention").  Steps:
+ *   1. kmean[b,h,:] = token mean of K (float32);
+ *   2. Q and K - kmean to INT8, one float32 scale per (b, h, 64-token block),
+ *      round to nearest even, codes in [-127, 127];
+ *   3. V to FP8 e4m3 (OCP e4m3fn) with one float32 scale per (b, h, channel);
+ *   4. S = (Q8 . K8) * sq * sk * scale on INT8 matrix cores, exact int32 sums;
+ *   5. online softmax over key tiles of fa_int8qk_kv_block() keys, P taken
+ *      against the running max and rounded to e4m3 as 448 * P; the
+ *      denominator sums the unrounded P;
+ *   6. O = (sum of P8 V8 on FP8 matrix cores, float32 accumulate) * sv / (448 l).
+ * Same tensor conventions as fa_fwd.  dtype F16 or BF16, D = 128.  Masks:
+ * NONE or KEYLEN (keys beyond the length are dropped after quantisation;
+ * kmean and the scales still run over all N tokens).
+ *   workspace        device scratch of at least
+ *                    fa_fwd_int8qk_workspace_bytes(B,H,N,D) bytes, 256-byte
+ *                    aligned; contents on entry are ignored.
+ */
+FA_API size_t fa_fwd_int8qk_workspace_bytes(int B, int H, int N, int D);
+FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                  fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                  void* hip_stream);
+
+/* Keys per tile of the quantised variant's online softmax (P is rounded
+ * against the running max, so the result depends on this tile size). */
+FA_API int fa_int8qk_kv_block(void);
+
+/* Static text for a status code. */
+FA_API const char* fa_status_string(int status);
+
+/* Text of the last HIP error seen by this thread (empty if none). */
+FA_API const char* fa_last_hip_error(void);
+
+/* ABI version: bumped whenever a signature or convention above changes. */
+FA_API int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,112 @@
+"""The C ABI library loads and exports what include/fa.h declares, and its
+host-side validation rejects bad arguments before touching the GPU (these
+calls return before any HIP runtime call, so they run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_fa_fwd_04_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# a fake but 256-byte aligned, never dereferenced, device address
+P = 1 << 20
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"FA_API\s+[\w\s\*]*?\b(fa_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    return fa.lib()
+
+
+def test_header_declares_the_python_names():
+    assert declared_functions() == sorted(fa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    # nothing but the C ABI is exported (templates and helpers stay hidden)
+    assert {e for e in exported if not e.startswith("_")} == set(declared_functions())
+
+
+def test_static_queries(lib):
+    assert fa.fa_abi_version() == 1
+    assert fa.fa_int8qk_kv_block() % 64 == 0
+    assert fa.fa_status_string(0) == "ok"
+    for code in range(-7, 0):
+        assert fa.fa_status_string(code) not in ("ok", "unknown status")
+    assert fa.fa_status_string(-99) == "unknown status"
+    assert fa.fa_last_hip_error() == ""
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, mask=None, B=1, H=2, N=64, D=128, scale=0.1, dtype=fa.FA_BF16,
+             hip_stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["mask"], a["B"], a["H"], a["N"], a["D"],
+                     a["scale"], a["dtype"], a["hip_stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_NULL), (dict(o=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(N=-3), fa.FA_ERR_SHAPE), (dict(D=0), fa.FA_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 20), fa.FA_ERR_SHAPE),
+    (dict(D=64), fa.FA_ERR_UNSUPPORTED), (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_ARG), (dict(scale=-1.0), fa.FA_ERR_ARG), (dict(scale=float("nan")), fa.FA_ERR_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_ARG),
+    (dict(k=P + 8), fa.FA_ERR_ALIGN), (dict(lse=P + 2), fa.FA_ERR_ALIGN),
+])
+def test_fwd_validation(lib, kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_mask_validation(lib):
+    bad_kind = fa.fa_mask_t(9, P, 0, 0, 0, 0)
+    assert _fwd(mask=ctypes.byref(bad_kind)) == fa.FA_ERR_ARG
+    null_ptr = fa.fa_mask_t(fa.FA_MASK_KEYLEN, None, 0, 0, 0, 0)
+    assert _fwd(mask=ctypes.byref(null_ptr)) == fa.FA_ERR_NULL
+    misaligned = fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P + 1, 0, 0, 64, 1)
+    assert _fwd(mask=ctypes.byref(misaligned)) == fa.FA_ERR_ALIGN
+    neg = fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P, 0, 0, -64, 1)
+    assert _fwd(mask=ctypes.byref(neg)) == fa.FA_ERR_ARG
+
+
+def test_int8qk_validation(lib):
+    ws = fa.fa_fwd_int8qk_workspace_bytes(1, 2, 1000, 128)
+    assert ws > 3 * 2 * 1000 * 128
+    assert fa.fa_fwd_int8qk_workspace_bytes(0, 2, 1000, 128) == 0
+
+    def call(**kw):
+        a = dict(dtype=fa.FA_BF16, D=128, ws=P, wsb=ws, mask=None)
+        a.update(kw)
+        return fa.fa_fwd_int8qk(P, P, P, P, None, a["mask"], 1, 2, 1000, a["D"], 0.1, a["dtype"],
+                                a["ws"], a["wsb"], None)
+
+    assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert call(D=40) == fa.FA_ERR_UNSUPPORTED
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=ws - 1) == fa.FA_ERR_WORKSPACE
+    assert call(ws=P + 16) == fa.FA_ERR_ALIGN
+    add = fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P, 0, 0, 0, 1)
+    assert call(mask=ctypes.byref(add)) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_wrapper_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 32)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)

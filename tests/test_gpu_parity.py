@@ -1,0 +1,229 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Element-by-element comparisons at sizes the oracle finishes in seconds (many
+tiles, ragged tails, every dtype / head dim / mask kind), and sampled rows at
+the full workload sizes in the launch configuration the benchmark times.
+
+Tolerances: float32 max |err| <= 1e-5; fp16 / bf16 max |err| <= 1e-2 and
+mean |err| <= 1e-3 (outputs rounded to the storage type; the oracle is fp64
+on the same rounded inputs).  lse: |err| <= 1e-5 (fp32) / 1e-4 (fp16, bf16).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_fa_fwd_04_amd as fa
+from attention_fa_fwd_04_amd.workloads import WORKLOADS, Workload, make_inputs, sample_rows
+from oracle import attention
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = {torch.float32: (1e-5, None), torch.float16: (1e-2, 1e-3), torch.bfloat16: (1e-2, 1e-3)}
+LSE_TOL = {torch.float32: 1e-5, torch.float16: 1e-4, torch.bfloat16: 1e-4}
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    fa.lib()
+    return torch.device("cuda", 0)
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def check_o(o_gpu, o_ref, dtype, what):
+    o = _f64(o_gpu)
+    err = np.abs(o - o_ref)
+    mx, mean_tol = O_TOL[dtype]
+    rel = np.sqrt((err ** 2).mean() / max((o_ref ** 2).mean(), 1e-300))
+    say(f"  {what}: max|err|={err.max():.3e} mean|err|={err.mean():.3e} relRMS={rel:.3e}")
+    assert np.isfinite(o).all(), what
+    assert err.max() <= mx, what
+    if mean_tol is not None:
+        assert err.mean() <= mean_tol, what
+
+
+def check_lse(lse_gpu, lse_ref, dtype, what):
+    l = _f64(lse_gpu)
+    assert np.array_equal(np.isneginf(l), np.isneginf(lse_ref)), what
+    fin = np.isfinite(lse_ref)
+    if fin.any():
+        err = np.abs(l[fin] - lse_ref[fin]).max()
+        say(f"  {what}: lse max|err|={err:.3e}")
+        assert err <= LSE_TOL[dtype], what
+
+
+def run(dev, inp, *, mask=None, key_len=None, scale=None):
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    kl = None if key_len is None else key_len.to(dev)
+    m = None if mask is None else mask.to(dev)
+    o, lse = fa.fwd(q, k, v, attn_mask=m, key_len=kl, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ------------------------------------------------------------------ small / full compare
+
+def test_worked_example_fp32(dev):
+    w = WORKLOADS[1]
+    inp = make_inputs(w)
+    o, lse = run(dev, inp)
+    ref_o, ref_l = attention.naive(inp["q"].numpy(), inp["k"].numpy(), inp["v"].numpy(), w.scale)
+    check_o(o, ref_o, torch.float32, "worked example")
+    check_lse(lse, ref_l, torch.float32, "worked example")
+
+
+SWEEP_N = [1, 33, 64, 129, 1000]
+
+
+@pytest.mark.parametrize("mask_kind", ["none", "keylen", "additive"])
+@pytest.mark.parametrize("D", [32, 40, 128])
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_sweep(dev, dt, D, mask_kind):
+    for N in SWEEP_N:
+        w = Workload(90 + D, f"sweep-{dt}", dt, 2, 3, N, D)
+        inp = make_inputs(w)
+        dtype = DT[dt]
+        kl = mask = None
+        if mask_kind == "keylen":
+            kl = torch.tensor([max(1, N // 2 + 1), N], dtype=torch.int32)
+        elif mask_kind == "additive":
+            g = np.random.default_rng(N * 7 + D)
+            mv = g.standard_normal((2, 1, N, N)) * 2.0
+            mv[g.random((2, 1, N, N)) < 0.2] = -np.inf
+            mask = torch.from_numpy(mv.astype(np.float32))
+        say(f"case dt={dt} D={D} N={N} mask={mask_kind}")
+        o, lse = run(dev, inp, mask=mask, key_len=kl)
+        ref_o, ref_l = attention.naive(inp["q"].double().numpy(), inp["k"].double().numpy(),
+                                       inp["v"].double().numpy(), w.scale,
+                                       mask=None if mask is None else mask.double().numpy(),
+                                       key_len=None if kl is None else kl.numpy())
+        check_o(o, ref_o, dtype, f"N={N}")
+        check_lse(lse, ref_l, dtype, f"N={N}")
+
+
+def test_fully_masked_rows(dev):
+    w = Workload(97, "masked", "bf16", 2, 2, 100, 128)
+    inp = make_inputs(w)
+    o, lse = run(dev, inp, key_len=torch.tensor([0, 37], dtype=torch.int32))
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    ref_o, ref_l = attention.naive(inp["q"][1:].double().numpy(), inp["k"][1:].double().numpy(),
+                                   inp["v"][1:].double().numpy(), w.scale, key_len=np.array([37]))
+    check_o(o[1:], ref_o, torch.bfloat16, "len 37")
+    # an additive mask that removes every key of some rows
+    mv = torch.zeros(1, 1, 100, 100)
+    mv[..., 5, :] = float("-inf")
+    o2, lse2 = run(dev, inp, mask=mv)
+    assert torch.all(o2[:, :, 5] == 0) and torch.all(torch.isneginf(lse2[:, :, 5]))
+
+
+def test_boolean_mask_wrapper(dev):
+    w = Workload(98, "boolmask", "f16", 1, 2, 150, 40)
+    inp = make_inputs(w)
+    keep = torch.from_numpy(np.random.default_rng(3).random((1, 2, 150, 150)) > 0.5)
+    o = fa.fwd(*(inp[n].to(dev) for n in ("q", "k", "v")), attn_mask=keep.to(dev))
+    add = np.where(keep.numpy(), 0.0, -np.inf)
+    ref_o, _ = attention.naive(inp["q"].double().numpy(), inp["k"].double().numpy(),
+                               inp["v"].double().numpy(), w.scale, mask=add)
+    check_o(o, ref_o, torch.float16, "bool mask")
+
+
+def test_scale_argument(dev):
+    w = Workload(99, "scale", "bf16", 1, 2, 300, 128)
+    inp = make_inputs(w)
+    o, lse = run(dev, inp, scale=0.02)
+    ref_o, ref_l = attention.naive(inp["q"].double().numpy(), inp["k"].double().numpy(),
+                                   inp["v"].double().numpy(), 0.02)
+    check_o(o, ref_o, torch.bfloat16, "scale 0.02")
+    check_lse(lse, ref_l, torch.bfloat16, "scale 0.02")
+
+
+def test_deterministic_and_in_bounds(dev):
+    """Bitwise identical reruns; guard bands around o and lse stay untouched."""
+    w = WORKLOADS[2].with_shape(H=4, N=1111)
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    B, H, N, D = q.shape
+    G = 4096
+    guard = torch.full((G + q.numel() + G,), 7.0, dtype=q.dtype, device=dev)
+    lguard = torch.full((G + B * H * N + G,), 7.0, dtype=torch.float32, device=dev)
+    o = guard[G:G + q.numel()].view(q.shape)
+    lse = lguard[G:G + B * H * N].view(B, H, N)
+    outs = []
+    for _ in range(3):
+        rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), None,
+                       B, H, N, D, w.scale, fa.FA_BF16, torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        outs.append((o.clone(), lse.clone()))
+    for oo, ll in outs[1:]:
+        assert torch.equal(oo.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(ll.view(torch.int32), outs[0][1].view(torch.int32))
+    assert torch.all(guard[:G] == 7) and torch.all(guard[-G:] == 7)
+    assert torch.all(lguard[:G] == 7) and torch.all(lguard[-G:] == 7)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sampled_check(dev, w, o, lse, inp, rows, key_len=None):
+    dtype = w.torch_dtype
+    errs, lerrs = [], []
+    o_c = o.cpu()
+    l_c = lse.cpu()
+    for (b, h) in sorted({(int(r[0]), int(r[1])) for r in rows}):
+        ids = rows[(rows[:, 0] == b) & (rows[:, 1] == h)][:, 2]
+        kh = inp["k"][b, h].double().numpy()
+        vh = inp["v"][b, h].double().numpy()
+        kl = None if key_len is None else int(key_len[b])
+        ref_o, ref_l = attention.rows(inp["q"][b, h, ids].double().numpy(), kh, vh, w.scale, key_len=kl)
+        errs.append(np.abs(o_c[b, h, ids].double().numpy() - ref_o))
+        lerrs.append(np.abs(l_c[b, h, ids].double().numpy() - ref_l))
+    err = np.concatenate([e.ravel() for e in errs])
+    lerr = np.concatenate([e.ravel() for e in lerrs])
+    mx, mean_tol = O_TOL[dtype]
+    say(f"  {w.name}: {len(rows)} rows max|err|={err.max():.3e} mean|err|={err.mean():.3e} lse={lerr.max():.3e}")
+    assert err.max() <= mx and err.mean() <= mean_tol
+    assert lerr.max() <= LSE_TOL[dtype]
+
+
+def test_flux_full(dev):
+    w = WORKLOADS[2]
+    say(f"case {w}")
+    inp = make_inputs(w)
+    o, lse = run(dev, inp)
+    rows = sample_rows(w, 512)
+    _sampled_check(dev, w, o, lse, inp, rows)
+    # two whole heads element by element
+    for h in (0, w.H - 1):
+        ref_o, ref_l = attention.naive(inp["q"][:, h:h + 1].double().numpy(), inp["k"][:, h:h + 1].double().numpy(),
+                                       inp["v"][:, h:h + 1].double().numpy(), w.scale)
+        check_o(o[:, h:h + 1], ref_o, torch.bfloat16, f"flux head {h}")
+
+
+def test_sd15_keylen_full(dev):
+    w = WORKLOADS[3]
+    say(f"case {w}")
+    inp = make_inputs(w)
+    o, lse = run(dev, inp, key_len=inp["key_len"])
+    rows = sample_rows(w, 544)
+    assert len({int(b) for b in rows[:, 0]}) == w.B
+    _sampled_check(dev, w, o, lse, inp, rows, key_len=inp["key_len"].numpy())
+
+
+def test_video_full(dev):
+    w = WORKLOADS[4]
+    say(f"case {w}")
+    inp = make_inputs(w)
+    o, lse = run(dev, inp)
+    rows = sample_rows(w, w.sampled_rows)
+    _sampled_check(dev, w, o, lse, inp, rows)

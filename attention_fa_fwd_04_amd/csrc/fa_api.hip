@@ -11,6 +11,10 @@
 #include "fa_fwd_kernel.hpp"
 #include "fa_int8qk.hpp"
 
+#ifndef FA_FWD_MIN_BLOCKS
+#define FA_FWD_MIN_BLOCKS 2   // workgroups per CU the register budget is sized for
+#endif
+
 namespace {
 
 thread_local char g_hip_err[256] = "";
@@ -78,7 +82,8 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   if (log_enabled())
     std::fprintf(stderr, "[fa] fa_fwd dtype=%s D=%d mask=%d B=%d H=%d N=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
                  sizeof(T) == 4 ? "f32" : "f16/bf16", D, MASK, B, H, N, grid, C::NT, C::BR, BC, 2 * C::BUF);
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, BC, MASK>), dim3(grid), dim3(C::NT), 0, st,
+  constexpr int MINB = FA_FWD_MIN_BLOCKS;
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, BC, MASK, MINB>), dim3(grid), dim3(C::NT), 0, st,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                      static_cast<T*>(o), lse, m, H, N, nqt, scale * fa::kLog2e);
   return record_launch("fa_fwd_kernel");

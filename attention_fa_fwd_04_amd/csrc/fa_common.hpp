@@ -108,6 +108,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return xcd * per + (xcd < rem ? xcd : rem) + k;
 }
 
+// Buffer resource over [base, base + bytes): loads at offsets outside the
+// range return zero instead of touching memory, so tails and masked rows
+// need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOobOffset = 0x80000000u;   // beyond any range this library builds
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 __device__ __forceinline__ float wave_max_halves(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
 }

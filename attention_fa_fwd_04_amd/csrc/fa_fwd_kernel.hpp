@@ -63,8 +63,10 @@ struct FwdCfg {
   static_assert(2 * BUF <= 160 * 1024, "double buffer must fit in LDS");
 };
 
-template <typename T, int D, int BC, int MASK>
-__global__ __launch_bounds__(256) void fa_fwd_kernel(
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
+template <typename T, int D, int BC, int MASK, int MINB>
+__global__ __launch_bounds__(256, MINB) void fa_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, MaskArgs mask,
     int H, int N, int nqt, float c_log2) {
@@ -79,9 +81,7 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
   const int bh = logical / nqt, qt = logical - bh * nqt;
   const int b = bh / H, h = bh - b * H;
   const size_t head_off = (size_t)bh * (size_t)N * D;
-  const uint8_t* Qh = reinterpret_cast<const uint8_t*>(Q + head_off);
-  const uint8_t* Kh = reinterpret_cast<const uint8_t*>(K + head_off);
-  const uint8_t* Vh = reinterpret_cast<const uint8_t*>(V + head_off);
+  constexpr uint32_t kRow = D * C::E;             // bytes per row
 
   int n_eff = N;
   if constexpr (MASK == kMaskLen) {
@@ -89,19 +89,21 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
     n_eff = L < 0 ? 0 : (L > N ? N : L);
   }
   const int ntiles = (n_eff + BC - 1) / BC;
+  // Rows at or past n_eff read as zero: K and V ranges end there.
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head_off, (uint32_t)N * kRow);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head_off, (uint32_t)n_eff * kRow);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head_off, (uint32_t)n_eff * kRow);
 
   const int q_row = qt * C::BR + wave * 32 + ln;
   const bool q_ok = q_row < N;
 
-  // Q in B-operand layout: step s, lane half h holds chunk 2s + h of its row.
+  // Q in B-operand layout: step s, lane half h holds chunk 2s + h of its row
+  // (chunks past D, and rows past N, read as zero).
   u32x4 qreg[C::QKS];
 #pragma unroll
   for (int s = 0; s < C::QKS; ++s) {
     const int ch = 2 * s + lh;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (q_ok && ch < C::DCH)
-      z = *reinterpret_cast<const u32x4*>(Qh + (size_t)q_row * (D * C::E) + ch * 16);
-    qreg[s] = z;
+    qreg[s] = buf_load16(qr, ch < C::DCH ? (uint32_t)q_row * kRow + ch * 16 : kOobOffset);
   }
 
   // Zero the padding the tile writes never touch: K chunks past D (QK steps
@@ -127,29 +129,23 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
   u32x4 kst[C::KIT];
   u32x4 vst[C::VIT][4];
 
+  // Loads past the last tile read zeros (outside the buffer range), so the
+  // prefetch needs no guard.
   auto load_tile = [&](int j) {
-    const int kv0 = j * BC;
+    const uint32_t base = (uint32_t)(j * BC) * kRow;
 #pragma unroll
     for (int i = 0; i < C::KIT; ++i) {
       const int it = tid + i * C::NT;
-      const int row = it / C::DCH;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (it < C::KITEMS && kv0 + row < n_eff)
-        z = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv0 * (D * C::E) + (size_t)it * 16);
-      kst[i] = z;
+      kst[i] = buf_load16(kr, (C::KITEMS % C::NT == 0 || it < C::KITEMS) ? base + it * 16 : kOobOffset);
     }
 #pragma unroll
     for (int i = 0; i < C::VIT; ++i) {
       const int it = tid + i * C::NT;
       const int kg = it % (BC / 4), dc = it / (BC / 4);
+      const bool ok = C::VITEMS % C::NT == 0 || it < C::VITEMS;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kv0 + 4 * kg + r;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (it < C::VITEMS && key < n_eff)
-          z = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * (D * C::E) + dc * 16);
-        vst[i][r] = z;
-      }
+      for (int r = 0; r < 4; ++r)
+        vst[i][r] = buf_load16(vr, ok ? base + (uint32_t)(4 * kg + r) * kRow + dc * 16 : kOobOffset);
     }
   };
 
@@ -159,7 +155,7 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < C::KIT; ++i) {
       const int it = tid + i * C::NT;
-      if (it < C::KITEMS) {
+      if (C::KITEMS % C::NT == 0 || it < C::KITEMS) {
         const int row = it / C::DCH, c = it - row * C::DCH;
         *reinterpret_cast<u32x4*>(kb + row * C::KSTR + c * 16) = kst[i];
       }
@@ -167,7 +163,7 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < C::VIT; ++i) {
       const int it = tid + i * C::NT;
-      if (it >= C::VITEMS) continue;
+      if (!(C::VITEMS % C::NT == 0 || it < C::VITEMS)) continue;
       const int kg = it % (BC / 4), dc = it / (BC / 4);
       const int key = 4 * kg;                       // first of 4 consecutive keys
       const int kk = key & 31;
@@ -192,7 +188,13 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
     }
   };
 
-  float m_run = -INFINITY;   // running max, log2 units
+  // Running state.  m_run is the reference the exponentials are taken
+  // against (log2 units); it is raised only when some row's max exceeds it
+  // by more than kLazy, so P <= 2^kLazy and the accumulator is rescaled
+  // rarely.  Normalising by l at the end makes the result independent of
+  // the reference.
+  constexpr float kLazy = 8.f;
+  float m_run = -INFINITY;
   float l_run = 0.f;         // this lane half's share of the denominator
   f32x16 acc[C::PVB];
 #pragma unroll
@@ -210,15 +212,13 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
            (int64_t)(q_ok ? q_row : 0) * mask.sq;
   }
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
+  // One K/V tile: scores, online softmax, P V.  MASKED adds the additive
+  // mask or drops keys at or past n_eff; it is only needed on the last tile
+  // unless the mask is additive.
+  auto step = [&](int j, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
+    load_tile(j + 1);
     const uint8_t* kb = smem + buf * C::BUF;
     const uint8_t* vb = kb + C::KBYTES;
     const int kv0 = j * BC;
@@ -236,27 +236,22 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
       }
     }
 
-    // mask, row max
-    if constexpr (kPre) {
+    if constexpr (MASKED) {
 #pragma unroll
       for (int G = 0; G < C::SB; ++G)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
           float t = -INFINITY;
-          if (key < N) {
-            const float mv = q_ok ? mrow[(int64_t)key * mask.sk] : 0.f;
-            t = __builtin_fmaf(s[G][i], c_log2, mv * kLog2e);
+          if constexpr (kPre) {
+            if (key < N) {
+              const float mv = q_ok ? mrow[(int64_t)key * mask.sk] : 0.f;
+              t = __builtin_fmaf(s[G][i], c_log2, mv * kLog2e);
+            }
+          } else {
+            t = key < n_eff ? s[G][i] : -INFINITY;
           }
           s[G][i] = t;
-        }
-    } else if (kv0 + BC > n_eff) {
-#pragma unroll
-      for (int G = 0; G < C::SB; ++G)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if (key >= n_eff) s[G][i] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -264,11 +259,18 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
     for (int G = 0; G < C::SB; ++G)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[G][i]);
-    mx = wave_max_halves(mx);
-    const float m_new = fmaxf(m_run, mx * cs);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    mx = wave_max_halves(mx) * cs;
+    if (__ballot(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int p = 0; p < C::PVB; ++p)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[p][i] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
     // P = exp2(S*c - m), row sum
     float psum = 0.f;
@@ -280,15 +282,7 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
         s[G][i] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-
-    // rescale the accumulator only when some row's max moved
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int p = 0; p < C::PVB; ++p)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[p][i] *= alpha;
-    }
+    l_run += psum;
 
     // O^T += V^T P^T
 #pragma unroll
@@ -308,8 +302,19 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(
       }
     }
 
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    store_tile(buf ^ 1);
     __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  if constexpr (kPre) {
+    for (int j = 0; j < ntiles; ++j) step(j, BoolTag<true>{});
+  } else {
+    const int nfull = n_eff / BC;
+    for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});
+    if (nfull < ntiles) step(nfull, BoolTag<true>{});
   }
 
   // ---- epilogue: O = acc / l, lse = ln 2 * (m + log2 l) ----

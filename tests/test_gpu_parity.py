@@ -5,8 +5,13 @@ tiles, ragged tails, every dtype / head dim / mask kind), and sampled rows at
 the full workload sizes in the launch configuration the benchmark times.
 
 Tolerances: float32 max |err| <= 1e-5; fp16 / bf16 max |err| <= 1e-2 and
-mean |err| <= 1e-3 (outputs rounded to the storage type; the oracle is fp64
-on the same rounded inputs).  lse: |err| <= 1e-5 (fp32) / 1e-4 (fp16, bf16).
+mean |err| <= 1e-3 (the oracle is fp64 on the same rounded inputs).  The
+output itself is stored in fp16 / bf16, and rounding the exact result to
+that type alone moves it by up to half an ulp, 2^-11 |O| (fp16) or 2^-8 |O|
+(bf16), which passes 1e-2 once |O| > 2.56 in bf16 (rows with few unmasked
+keys); the max bound is therefore 1e-2 + that half ulp.  For the workloads'
+N(0, 1) inputs |O| stays far below 1 and the plain 1e-2 is what binds.
+lse: |err| <= 1e-5 (fp32) / 1e-4 (fp16, bf16).
 """
 import sys
 
@@ -21,6 +26,7 @@ from oracle import attention
 pytestmark = pytest.mark.gpu
 
 O_TOL = {torch.float32: (1e-5, None), torch.float16: (1e-2, 1e-3), torch.bfloat16: (1e-2, 1e-3)}
+HALF_ULP = {torch.float32: 0.0, torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
 LSE_TOL = {torch.float32: 1e-5, torch.float16: 1e-4, torch.bfloat16: 1e-4}
 DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -48,7 +54,7 @@ def check_o(o_gpu, o_ref, dtype, what):
     rel = np.sqrt((err ** 2).mean() / max((o_ref ** 2).mean(), 1e-300))
     say(f"  {what}: max|err|={err.max():.3e} mean|err|={err.mean():.3e} relRMS={rel:.3e}")
     assert np.isfinite(o).all(), what
-    assert err.max() <= mx, what
+    assert np.all(err <= mx + HALF_ULP[dtype] * np.abs(o_ref)), what
     if mean_tol is not None:
         assert err.mean() <= mean_tol, what
 
@@ -192,7 +198,7 @@ def _sampled_check(dev, w, o, lse, inp, rows, key_len=None):
     lerr = np.concatenate([e.ravel() for e in lerrs])
     mx, mean_tol = O_TOL[dtype]
     say(f"  {w.name}: {len(rows)} rows max|err|={err.max():.3e} mean|err|={err.mean():.3e} lse={lerr.max():.3e}")
-    assert err.max() <= mx and err.mean() <= mean_tol
+    assert err.max() <= mx and err.mean() <= mean_tol          # |O| << 1 here: plain bound
     assert lerr.max() <= LSE_TOL[dtype]
 
 

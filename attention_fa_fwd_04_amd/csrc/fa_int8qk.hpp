@@ -1,4 +1,22 @@
-// INT8-QK / FP8-PV attention variant: workspace layout and launcher.
+// INT8-QK / FP8-PV attention variant (handbook page "算子加速：注意力、编译与融合",
+// section "SageAttention": K smoothed by its mean, Q and K quantised to INT8
+// so Q K^T runs on integer matrix cores, P and V in FP8).
+//
+// Four prepass launches and the main kernel, all on the caller's stream:
+//   int8_stats      per (b,h, 512-token split): float64 partial sums of K and
+//                   partial max |V| per channel (fixed order, no atomics)
+//   int8_finalize   per (b,h): kmean = fp32(sum / N); V scale av/448 and 448/av
+//   int8_quant_qk   per (b,h, 64-token block, Q or K): X = Q or fp32(K - kmean),
+//                   a = max |X|, codes rint(fp32(X * fp32(127/a))) in [-127,127],
+//                   scale fp32(a/127)
+//   int8_quant_v    per (b,h, 64-token block): e4m3(fp32(V * fp32(448/av))),
+//                   written transposed as V^T[d][key] with the key order of
+//                   each 64-key group permuted to match the P operand
+//   fa_int8qk       the online-softmax loop: S = (Q8 K8^T) * sq * sk * scale
+//                   from exact int32 sums; P against the exact running max
+//                   (no lazy rescale: P <= 1 is what makes the x448 FP8 scale
+//                   valid), rounded to e4m3 as 448 P; l sums the unrounded
+//                   448 P; O = acc * sv / l.
 #pragma once
 
 #include "fa_common.hpp"
@@ -8,8 +26,8 @@ namespace fa {
 
 constexpr int kInt8Bc = 64;        // keys per tile of the online softmax
 constexpr int kQBlock = 64;        // tokens per INT8 scale block
-constexpr int kStatRows = 512;     // tokens per partial-statistics workgroup
-constexpr int kMaxSplits = 256;
+constexpr int kStatRows = 512;     // tokens per partial-statistics workgroup (at least)
+constexpr int kMaxSplits = 1024;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -17,8 +35,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Int8Layout {
   int npad;          // N rounded up to kQBlock
   int groups;        // npad / kQBlock
-  int splits;        // token splits of the K-mean / V-absmax reduction
-  size_t q8, k8, v8t, sq, sk, sv, kpart, vpart, kmean;
+  int splits;        // token splits of the K-sum / V-absmax reduction
+  int split_rows;    // tokens per split
+  size_t q8, k8, v8t, sq, sk, sv, vmul, kmean, kpart, vpart;
   size_t total;
 };
 
@@ -29,25 +48,402 @@ inline Int8Layout int8qk_workspace_layout(int B, int H, int N, int D) {
   L.groups = L.npad / kQBlock;
   L.splits = (N + kStatRows - 1) / kStatRows;
   if (L.splits > kMaxSplits) L.splits = kMaxSplits;
+  L.split_rows = (N + L.splits - 1) / L.splits;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
-  L.q8 = take(bh * L.npad * D);                 // int8 [BH, npad, D]
-  L.k8 = take(bh * L.npad * D);                 // int8 [BH, npad, D]
-  L.v8t = take(bh * (size_t)D * L.npad);        // e4m3 [BH, D, npad], keys permuted per 64
-  L.sq = take(bh * L.groups * 4);               // f32 [BH, groups]
+  L.q8 = take(bh * L.npad * D);                    // int8 [BH, npad, D]
+  L.k8 = take(bh * L.npad * D);                    // int8 [BH, npad, D]
+  L.v8t = take(bh * (size_t)D * L.npad);           // e4m3 [BH, D, npad]
+  L.sq = take(bh * L.groups * 4);                  // f32 [BH, groups]
   L.sk = take(bh * L.groups * 4);
-  L.sv = take(bh * (size_t)D * 4);              // f32 [BH, D]
-  L.kpart = take(bh * (size_t)L.splits * D * 4);  // f32 [BH, splits, D] partial sums of K
-  L.vpart = take(bh * (size_t)L.splits * D * 4);  // f32 [BH, splits, D] partial max |V|
-  L.kmean = take(bh * (size_t)D * 4);           // f32 [BH, D]
+  L.sv = take(bh * (size_t)D * 4);                 // f32 [BH, D]  av / 448
+  L.vmul = take(bh * (size_t)D * 4);               // f32 [BH, D]  448 / av
+  L.kmean = take(bh * (size_t)D * 4);              // f32 [BH, D]
+  L.kpart = take(bh * (size_t)L.splits * D * 8);   // f64 [BH, splits, D]
+  L.vpart = take(bh * (size_t)L.splits * D * 4);   // f32 [BH, splits, D]
   L.total = off;
   return L;
 }
 
+// Position of key k (0..63) inside its 64-key group of V^T.  The P operand of
+// the FP8 32x32x64 MFMA takes, from lane half h, the 32 scores it holds for
+// the group in accumulator order: slot e = 16G + 4g + r is key 32G + 8g + 4h + r.
+// V^T row d stores at position 32h + e the key that slot pairs with.
+__host__ __device__ constexpr int v8_pos(int k) {
+  return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
+}
+
+// ---------------------------------------------------------------- prepass
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void int8_stats_kernel(
+    const T* __restrict__ K, const T* __restrict__ V, double* __restrict__ kpart,
+    float* __restrict__ vpart, int N, int splits, int split_rows) {
+  static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
+  constexpr int CH = D / 8;                     // 16-byte chunks per row
+  constexpr int RG = 256 / CH;                  // row groups
+  __shared__ double ssum[RG][D];
+  __shared__ float smax[RG][D];
+  const int s = blockIdx.x, bh = blockIdx.y;
+  const int c = threadIdx.x % CH, rg = threadIdx.x / CH;
+  const size_t head = (size_t)bh * N * D;
+  const int r0 = s * split_rows, r1 = min(N, r0 + split_rows);
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = r0 + rg; r < r1; r += RG) {
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(K + head + (size_t)r * D + c * 8);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(V + head + (size_t)r * D + c * 8);
+    const T* kt = reinterpret_cast<const T*>(&kv);
+    const T* vt = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[e] += (double)(float)kt[e];
+      mx[e] = fmaxf(mx[e], fabsf((float)vt[e]));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ssum[rg][c * 8 + e] = acc[e];
+    smax[rg][c * 8 + e] = mx[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    double t = 0;
+    float m = 0;
+    for (int g = 0; g < RG; ++g) {
+      t += ssum[g][d];
+      m = fmaxf(m, smax[g][d]);
+    }
+    kpart[((size_t)bh * splits + s) * D + d] = t;
+    vpart[((size_t)bh * splits + s) * D + d] = m;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void int8_finalize_kernel(
+    const double* __restrict__ kpart, const float* __restrict__ vpart, float* __restrict__ kmean,
+    float* __restrict__ sv, float* __restrict__ vmul, int N, int splits) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  double t = 0;
+  float m = 0;
+  for (int s = 0; s < splits; ++s) {
+    t += kpart[((size_t)bh * splits + s) * D + d];
+    m = fmaxf(m, vpart[((size_t)bh * splits + s) * D + d]);
+  }
+  kmean[(size_t)bh * D + d] = (float)(t / (double)N);
+  sv[(size_t)bh * D + d] = m > 0.f ? m / 448.f : 0.f;
+  vmul[(size_t)bh * D + d] = m > 0.f ? 448.f / m : 0.f;
+}
+
+// One 64-token block of Q (blockIdx.z == 0) or K - kmean (blockIdx.z == 1).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void int8_quant_qk_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ kmean,
+    int8_t* __restrict__ q8, int8_t* __restrict__ k8, float* __restrict__ sq, float* __restrict__ sk,
+    int N, int npad, int groups) {
+  static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
+  constexpr int CH = D / 8;
+  __shared__ float wmax[4];
+  const int g = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z;
+  const T* X = (isk ? K : Q) + (size_t)bh * N * D;
+  int8_t* X8 = (isk ? k8 : q8) + (size_t)bh * npad * D;
+  const int t = threadIdx.x;
+  float x[4][8];
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int it = t + 256 * i;              // 64 rows x 16 chunks
+    const int row = g * kQBlock + it / CH, c = it % CH;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (row < N) raw = *reinterpret_cast<const u32x4*>(X + (size_t)row * D + c * 8);
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float f = (float)v[e];
+      if (isk && row < N) f = f - kmean[(size_t)bh * D + c * 8 + e];
+      x[i][e] = f;
+      a = fmaxf(a, fabsf(f));
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+  if ((t & 63) == 0) wmax[t >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float inv = a > 0.f ? 127.f / a : 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int it = t + 256 * i;
+    const int row = g * kQBlock + it / CH, c = it % CH;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float r = __builtin_rintf(x[i][e] * inv);
+      r = fminf(fmaxf(r, -127.f), 127.f);
+      w[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
+    }
+    *reinterpret_cast<u32x2*>(X8 + (size_t)row * D + c * 8) = u32x2{w[0], w[1]};
+  }
+  if (t == 0) (isk ? sk : sq)[(size_t)bh * groups + g] = a > 0.f ? a / 127.f : 0.f;
+}
+
+// One 64-token block of V -> e4m3, transposed into V^T[d][64g + v8_pos(k)].
+template <typename T, int D>
+__global__ __launch_bounds__(256) void int8_quant_v_kernel(
+    const T* __restrict__ V, const float* __restrict__ vmul, uint8_t* __restrict__ v8t,
+    int N, int npad) {
+  static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
+  constexpr int TS = 64 + 16;                   // LDS row: 64 keys + pad
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * TS];
+  const int g = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const T* Vh = V + (size_t)bh * N * D;
+  // thread: key k = t / 4, channels 32 * (t % 4) .. +31
+  const int k = t >> 2, c0 = 32 * (t & 3);
+  const int row = g * kQBlock + k;
+  const int pos = v8_pos(k);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (row < N) raw = *reinterpret_cast<const u32x4*>(Vh + (size_t)row * D + c0 + 8 * q);
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int d = c0 + 8 * q + e;
+      const float y0 = (float)v[e] * vmul[(size_t)bh * D + d];
+      const float y1 = (float)v[e + 1] * vmul[(size_t)bh * D + d + 1];
+      const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      tile[d * TS + pos] = (uint8_t)(pk & 0xFF);
+      tile[(d + 1) * TS + pos] = (uint8_t)((pk >> 8) & 0xFF);
+    }
+  }
+  __syncthreads();
+  // thread: channel d = t / 2, 32 positions (t % 2)
+  const int d = t >> 1, half = t & 1;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + d * TS + 32 * half);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + d * TS + 32 * half + 16);
+  uint8_t* dst = v8t + ((size_t)bh * D + d) * npad + (size_t)g * kQBlock + 32 * half;
+  *reinterpret_cast<u32x4*>(dst) = lo;
+  *reinterpret_cast<u32x4*>(dst + 16) = hi;
+}
+
+// ---------------------------------------------------------------- main kernel
+//
+// Same work split as fa_fwd_kernel: 4 waves x 32 query rows, S^T = K Q^T so a
+// lane owns one query.  QK^T: v_mfma_i32_32x32x32_i8 (lane half h feeds the
+// 16 bytes of chunk 2s + h of its row, as in the 16-bit kernel).  PV:
+// v_mfma_f32_32x32x64_f8f6f4 on e4m3 operands, one instruction per 32
+// channels per 64-key tile.
+
+template <typename T, int MASKLEN>
+__global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
+    const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
+    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
+    const int* __restrict__ key_len, T* __restrict__ O, float* __restrict__ LSE,
+    int H, int N, int npad, int groups, int nqt, float c_log2) {
+  constexpr int D = 128, BC = kInt8Bc, BR = 128, NT = 256;
+  constexpr int KSTR = D + 16;                  // int8 K row + pad
+  constexpr int VSTR = BC + 16;                 // e4m3 V^T row (64 keys) + pad
+  constexpr int KBYTES = BC * KSTR, VBYTES = D * VSTR, BUF = KBYTES + VBYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 31, lh = lane >> 5;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / nqt, qt = logical - bh * nqt;
+  const int b = bh / H;
+
+  int n_eff = N;
+  if constexpr (MASKLEN) {
+    const int L = key_len[b];
+    n_eff = L < 0 ? 0 : (L > N ? N : L);
+  }
+  const int ntiles = (n_eff + BC - 1) / BC;
+
+  const int8_t* Qh = q8 + (size_t)bh * npad * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k8 + (size_t)bh * npad * D, (uint32_t)npad * D);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(v8t + (size_t)bh * D * npad, (uint32_t)D * npad);
+
+  const int q_row = qt * BR + wave * 32 + ln;
+  const bool q_ok = q_row < N;
+  // rows past N are zero codes in the workspace (npad >= q_row + 1 within the tile)
+  u32x4 qreg[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    qreg[s] = *reinterpret_cast<const u32x4*>(Qh + (size_t)min(q_row, npad - 1) * D + (2 * s + lh) * 16);
+  // every query of a wave lies in one 64-token scale block
+  const float sq_w = sq[(size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)];
+  const float* skh = sk + (size_t)bh * groups;
+
+  // staging: K tile 64 rows x 8 chunks, V^T tile 128 rows x 4 chunks -> 2 + 2 per thread
+  u32x4 kst[2], vst[2];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int it = tid + NT * i;
+      kst[i] = buf_load16(kr, (uint32_t)(j * BC) * D + it * 16);
+      const int d = it >> 2, c = it & 3;
+      vst[i] = buf_load16(vr, (uint32_t)d * npad + j * BC + c * 16);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint8_t* kb = smem + buf * BUF;
+    uint8_t* vb = kb + KBYTES;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int it = tid + NT * i;
+      *reinterpret_cast<u32x4*>(kb + (it >> 3) * KSTR + (it & 7) * 16) = kst[i];
+      *reinterpret_cast<u32x4*>(vb + (it >> 2) * VSTR + (it & 3) * 16) = vst[i];
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[p][i] = 0.f;
+  constexpr float kLog2_448 = 8.807354922057604f;
+
+  auto step = [&](int j, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int buf = j & 1;
+    load_tile(j + 1);
+    const uint8_t* kb = smem + buf * BUF;
+    const uint8_t* vb = kb + KBYTES;
+    const int kv0 = j * BC;
+    const float c = sq_w * skh[j] * c_log2;       // one K scale block per tile
+
+    i32x16 si[2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) si[G][i] = 0;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * G + ln) * KSTR + (2 * st + lh) * 16);
+        si[G] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                      __builtin_bit_cast(i32x4, qreg[st]), si[G], 0, 0, 0);
+      }
+    }
+    float s[32];
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float t = (float)si[G][i] * c;
+        if constexpr (MASKED) {
+          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
+          if (key >= n_eff) t = -INFINITY;
+        }
+        s[16 * G + i] = t;
+      }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, s[i]);
+    mx = wave_max_halves(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+      l_run *= alpha;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[p][i] *= alpha;
+    }
+    // 448 P = exp2(s - m + log2 448) <= 448; the FP8 operand is its e4m3 rounding
+    const float moff = m_use - kLog2_448;
+    float psum = 0.f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      const float p0 = __builtin_amdgcn_exp2f(s[i] - moff);
+      const float p1 = __builtin_amdgcn_exp2f(s[i + 1] - moff);
+      const float p2 = __builtin_amdgcn_exp2f(s[i + 2] - moff);
+      const float p3 = __builtin_amdgcn_exp2f(s[i + 3] - moff);
+      psum += (p0 + p1) + (p2 + p3);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+      pk[i >> 2] = (uint32_t)w;
+    }
+    l_run += psum;
+    const i32x8 bop = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3],
+                       (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint8_t* vrow = vb + (32 * p + ln) * VSTR + 32 * lh;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(vrow);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(vrow + 16);
+      const i32x8 aop = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      acc[p] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[p], 0, 0, 0, 0, 0, 0);
+    }
+    store_tile(buf ^ 1);
+    __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  const int nfull = n_eff / BC;
+  for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});
+  if (nfull < ntiles) step(nfull, BoolTag<true>{});
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_ok) {
+    T* orow = O + ((size_t)bh * N + q_row) * D;
+    const float* svh = sv + (size_t)bh * D;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * p + 8 * g + 4 * lh;
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(svh + d0);
+        store4<T>(orow + d0, acc[p][4 * g] * s4.x * inv, acc[p][4 * g + 1] * s4.y * inv,
+                  acc[p][4 * g + 2] * s4.z * inv, acc[p][4 * g + 3] * s4.w * inv);
+      }
+    if (LSE != nullptr && lh == 0)
+      LSE[(size_t)bh * N + q_row] =
+          l_tot > 0.f ? (m_run + log2f(l_tot) - kLog2_448) * kLn2 : -INFINITY;
+  }
+}
+
 template <typename T>
-int launch_int8qk(const void*, const void*, const void*, void*, float*, const int*,
-                  int, int, int, float, void*, const Int8Layout&, hipStream_t) {
-  return FA_ERR_UNSUPPORTED;
+int launch_int8qk(const void* q, const void* k, const void* v, void* o, float* lse, const int* key_len,
+                  int B, int H, int N, float scale, void* workspace, const Int8Layout& L, hipStream_t st) {
+  constexpr int D = 128;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* q8 = reinterpret_cast<int8_t*>(ws + L.q8);
+  int8_t* k8 = reinterpret_cast<int8_t*>(ws + L.k8);
+  uint8_t* v8t = ws + L.v8t;
+  float* sq = reinterpret_cast<float*>(ws + L.sq);
+  float* sk = reinterpret_cast<float*>(ws + L.sk);
+  float* sv = reinterpret_cast<float*>(ws + L.sv);
+  float* vmul = reinterpret_cast<float*>(ws + L.vmul);
+  float* kmean = reinterpret_cast<float*>(ws + L.kmean);
+  double* kpart = reinterpret_cast<double*>(ws + L.kpart);
+  float* vpart = reinterpret_cast<float*>(ws + L.vpart);
+  const T* Q = static_cast<const T*>(q);
+  const T* K = static_cast<const T*>(k);
+  const T* V = static_cast<const T*>(v);
+  const int BH = B * H;
+  hipLaunchKernelGGL((int8_stats_kernel<T, D>), dim3(L.splits, BH), dim3(256), 0, st, K, V, kpart, vpart, N, L.splits,
+                     L.split_rows);
+  hipLaunchKernelGGL((int8_finalize_kernel<D>), dim3(BH), dim3(D), 0, st, kpart, vpart, kmean, sv, vmul, N, L.splits);
+  hipLaunchKernelGGL((int8_quant_qk_kernel<T, D>), dim3(L.groups, BH, 2), dim3(256), 0, st, Q, K, kmean, q8, k8, sq, sk,
+                     N, L.npad, L.groups);
+  hipLaunchKernelGGL((int8_quant_v_kernel<T, D>), dim3(L.groups, BH), dim3(256), 0, st, V, vmul, v8t, N, L.npad);
+  const int nqt = (N + 127) / 128;
+  const int grid = BH * nqt;
+  if (key_len)
+    hipLaunchKernelGGL((fa_int8qk_kernel<T, 1>), dim3(grid), dim3(256), 0, st, q8, k8, v8t, sq, sk, sv, key_len,
+                       static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
+  else
+    hipLaunchKernelGGL((fa_int8qk_kernel<T, 0>), dim3(grid), dim3(256), 0, st, q8, k8, v8t, sq, sk, sv, key_len,
+                       static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
+  return FA_OK;
 }
 
 }  // namespace fa

@@ -98,12 +98,30 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
  *      against the running max and rounded to e4m3 as 448 * P; the
  *      denominator sums the unrounded P;
  *   6. O = (sum of P8 V8 on FP8 matrix cores, float32 accumulate) * sv / (448 l).
+ * lse (if requested) is that of the smoothed, quantised scores in step 4: it
+ * differs from the unquantised row log-sum-exp by -scale * q . kmean (the
+ * per-row constant smoothing removes) plus quantisation error.
  * Same tensor conventions as fa_fwd.  dtype F16 or BF16, D = 128.  Masks:
  * NONE or KEYLEN (keys beyond the length are dropped after quantisation;
  * kmean and the scales still run over all N tokens).
  *   workspace        device scratch of at least
  *                    fa_fwd_int8qk_workspace_bytes(B,H,N,D) bytes, 256-byte
- *                    aligned; contents on entry are ignored.
+ *                    aligned; contents on entry are ignored.  On return it
+ *                    holds the quantised operands, each region starting at
+ *                    the next 256-byte boundary, in this order (Np = N rounded
+ *                    up to 64, BH = B*H):
+ *                      q8    int8  [BH, Np, D]   (rows >= N are 0)
+ *                      k8    int8  [BH, Np, D]
+ *                      v8t   e4m3  [BH, D, Np]   row d, position 64g + pi(k)
+ *                            holds key 64g + k, pi(k) = 32*((k>>2)&1) +
+ *                            16*(k>>5) + 4*((k>>3)&3) + (k&3)
+ *                      sq    f32   [BH, Np/64]   Q scale per 64-token block
+ *                      sk    f32   [BH, Np/64]   K scale per 64-token block
+ *                      sv    f32   [BH, D]       V scale (absmax / 448)
+ *                      vmul  f32   [BH, D]       448 / absmax
+ *                      kmean f32   [BH, D]
+ *                    followed by reduction scratch.  Calls that share a
+ *                    workspace must be ordered on one stream.
  */
 FA_API size_t fa_fwd_int8qk_workspace_bytes(int B, int H, int N, int D);
 FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -66,26 +66,44 @@ def e4m3_bits_to_f64(bits) -> np.ndarray:
 _E4M3_POS = e4m3_bits_to_f64(np.arange(0, 0x7F, dtype=np.uint8))
 
 
-def f64_to_e4m3_bits(x) -> np.ndarray:
-    """Round to the nearest e4m3fn value (ties to the even code), saturating at 448."""
+def e4m3_nearest_by_search(x) -> np.ndarray:
+    """Round to the nearest e4m3fn value (ties to the even code), saturating at
+    448, by searching the table of all finite values.  Slow; used to pin
+    ``round_e4m3``."""
     x = np.asarray(x, dtype=np.float64)
-    a = np.abs(x)
-    sat = a >= E4M3_MAX
-    a_c = np.minimum(a, E4M3_MAX)
-    hi = np.searchsorted(_E4M3_POS, a_c, side="left")          # first value >= a
-    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.minimum(np.searchsorted(_E4M3_POS, a, side="left"), len(_E4M3_POS) - 1)
     lo = np.maximum(hi - 1, 0)
     vhi, vlo = _E4M3_POS[hi], _E4M3_POS[lo]
-    dhi, dlo = vhi - a_c, a_c - vlo
-    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo)
-    code = np.where(vhi == a_c, hi, code)
-    code = np.where(sat, 0x7E, code).astype(np.uint8)
-    sign = np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
-    out = code | sign
-    return np.where(np.isnan(x), np.uint8(0x7F), out).astype(np.uint8)
+    dhi, dlo = vhi - a, a - vlo
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)) | (vhi == a)
+    v = np.where(pick_hi, vhi, vlo)
+    v = np.where(np.signbit(x), -v, v)
+    return np.where(np.isnan(x), np.nan, v)
 
 
 def round_e4m3(x) -> np.ndarray:
-    """Value of x after rounding to e4m3fn (saturating), as float64."""
-    return e4m3_bits_to_f64(f64_to_e4m3_bits(x))
+    """Value of x after rounding to e4m3fn (ties to even, saturating at 448), as float64.
+
+    Within a binade [2^e, 2^(e+1)) with e >= -6 the e4m3 values are spaced
+    2^(e-3) (3 mantissa bits); below 2^-6 (subnormals) the spacing is 2^-9.
+    Dividing by the spacing, rounding half to even and multiplying back is
+    exact in float64.  Results beyond 448 saturate to 448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 2.0 * E4M3_MAX)   # keeps the exponent field finite
+    e = (a.view(np.uint64) >> np.uint64(52)).astype(np.int64) - 1023   # binade of a
+    e = np.maximum(e, -6)                     # subnormal range shares the 2^-6 spacing
+    quantum = ((e - 3 + 1023).astype(np.uint64) << np.uint64(52)).view(np.float64)
+    r = np.rint(a / quantum) * quantum
+    r = np.minimum(r, E4M3_MAX)
+    r = np.where(np.signbit(x), -r, r)
+    return np.where(np.isnan(x), np.nan, r)
+
+
+def f64_to_e4m3_bits(x) -> np.ndarray:
+    """e4m3fn bit patterns of round_e4m3(x)."""
+    v = round_e4m3(x)
+    a = np.abs(v)
+    code = np.searchsorted(_E4M3_POS, np.nan_to_num(a)).astype(np.uint8)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(v), np.uint8(0x7F), code | sign).astype(np.uint8)

@@ -49,19 +49,18 @@ def k_mean(k_head) -> np.ndarray:
 def quantise_int8_blocks(x_head, block=QBLOCK):
     """x_head [N, D] (float32 values) -> (x8 int8 [N, D], scale float32 [ceil(N/block)])."""
     x = np.asarray(x_head, dtype=np.float32)
-    n = x.shape[0]
+    n, d = x.shape
     nb = -(-n // block)
-    x8 = np.zeros(x.shape, dtype=np.int8)
-    sc = np.zeros(nb, dtype=np.float32)
-    for g in range(nb):
-        xb = x[g * block:(g + 1) * block]
-        a = np.float32(np.abs(xb).max()) if xb.size else np.float32(0)
-        if a == 0:
-            continue
-        inv = np.float32(np.float32(127.0) / a)
-        y = (xb * inv).astype(np.float32)
-        x8[g * block:(g + 1) * block] = np.clip(np.rint(y), -127, 127).astype(np.int8)
-        sc[g] = np.float32(a / np.float32(127.0))
+    xp = np.zeros((nb * block, d), dtype=np.float32)
+    xp[:n] = x
+    xb = xp.reshape(nb, block * d)
+    a = np.abs(xb).max(axis=1).astype(np.float32)               # per-block absmax
+    live = a > 0
+    safe = np.where(live, a, np.float32(1)).astype(np.float32)
+    inv = np.where(live, (np.float32(127.0) / safe).astype(np.float32), np.float32(0)).astype(np.float32)
+    y = (xb * inv[:, None]).astype(np.float32)
+    x8 = np.clip(np.rint(y), -127, 127).astype(np.int8).reshape(nb * block, d)[:n]
+    sc = np.where(live, (a / np.float32(127.0)).astype(np.float32), np.float32(0)).astype(np.float32)
     return x8, sc
 
 
@@ -87,8 +86,10 @@ def quantise_head(q_head, k_head, v_head):
     return dict(kmean=km, ks=ks, q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv)
 
 
-def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quantise_p=True):
-    """Blocked recurrence over key tiles with P quantised against the running max."""
+def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quantise_p=True,
+                              return_lse=False):
+    """Blocked recurrence over key tiles with P quantised against the running max.
+    The lse is that of the quantised, smoothed scores (natural log)."""
     row_ids = np.asarray(row_ids, dtype=np.int64)
     q8 = qz["q8"][row_ids].astype(np.float64)
     k8 = qz["k8"].astype(np.float64)
@@ -116,24 +117,30 @@ def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quanti
         m = m_new
     with np.errstate(invalid="ignore", divide="ignore"):
         o = acc * qz["sv"].astype(np.float64)[None, :] / (E4M3_MAX * l)
-    return np.where(l == 0, 0.0, o)
+        lse = np.where(l[:, 0] == 0, -np.inf, m[:, 0] + np.log(l[:, 0]))
+    o = np.where(l == 0, 0.0, o)
+    return (o, lse) if return_lse else o
 
 
-def emulate_rows(q_head, k_head, v_head, row_ids, scale, kv_block, key_len=None, qz=None):
+def emulate_rows(q_head, k_head, v_head, row_ids, scale, kv_block, key_len=None, qz=None,
+                 return_lse=False):
     """Quantised-variant output for selected query rows of one head (float64, before
-    the output rounding)."""
+    the output rounding); with return_lse also the rows' log-sum-exp of the
+    smoothed quantised scores."""
     if qz is None:
         qz = quantise_head(q_head, k_head, v_head)
-    return _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len)
+    return _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len, return_lse=return_lse)
 
 
-def emulate(q, k, v, scale, kv_block, key_len=None):
+def emulate(q, k, v, scale, kv_block, key_len=None, return_lse=False):
     """Full [B, H, N, D] emulation (small shapes)."""
     q = np.asarray(q)
     B, H, N, D = q.shape
     out = np.zeros((B, H, N, np.asarray(v).shape[3]))
+    lse = np.zeros((B, H, N))
     for b in range(B):
         for h in range(H):
             kl = None if key_len is None else int(np.asarray(key_len)[b])
-            out[b, h] = emulate_rows(q[b, h], k[b, h], v[b, h], np.arange(N), scale, kv_block, kl)
-    return out
+            out[b, h], lse[b, h] = emulate_rows(q[b, h], k[b, h], v[b, h], np.arange(N), scale, kv_block,
+                                                kl, return_lse=True)
+    return (out, lse) if return_lse else out

@@ -73,6 +73,20 @@ def test_e4m3_rounding_matches_torch_in_range():
         assert np.array_equal(ref, got)
 
 
+def test_e4m3_grid_rounding_matches_table_search():
+    """The binade-grid rounding equals a nearest-value search over the table of
+    every finite e4m3 value (ties to the even code)."""
+    rng = np.random.default_rng(5)
+    pos = rounding.e4m3_bits_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[1:] + pos[:-1]) / 2
+    x = np.concatenate([rng.uniform(-500, 500, 1 << 18), rng.standard_normal(1 << 16) * 2.0 ** -7,
+                        mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9), pos, -pos,
+                        [448.0, 464.0, 1e9, -1e9, 0.0, -0.0]])
+    assert np.array_equal(rounding.round_e4m3(x), rounding.e4m3_nearest_by_search(x))
+    codes = rounding.f64_to_e4m3_bits(x)
+    assert np.array_equal(rounding.e4m3_bits_to_f64(codes), rounding.round_e4m3(x))
+
+
 def test_e4m3_saturates():
     x = np.array([448.0, 449.0, 463.9, 464.0, 1e6, -1e6, np.inf])
     assert np.array_equal(rounding.round_e4m3(x), [448, 448, 448, 448, 448, -448, 448])

@@ -121,6 +121,25 @@ def test_identity_quantisers_reduce_to_blocked_oracle():
     assert np.abs(o_id - o_bl[0, 0]).max() < 1e-12
 
 
+def test_emulated_lse_is_that_of_smoothed_scores():
+    """In the lossless construction the emulated lse equals the unquantised lse
+    of (Q, K - kmean); with K's mean nonzero it equals the unquantised lse of
+    (Q, K) minus scale * q . kmean (softmax's shift invariance)."""
+    q, k, v, step_q, step_k = _lossless_head(5)
+    scale = math.log(2) / (step_q * step_k)
+    n = len(q)
+    _, lse = sage.emulate_rows(q, k, v, np.arange(n), scale, 64, return_lse=True)
+    _, ref = attention.naive(q[None, None], k[None, None], v[None, None], scale)
+    assert np.abs(lse - ref[0, 0]).max() < 1e-9
+    rng = np.random.default_rng(9)
+    q2, k2, v2 = (rng.standard_normal((150, 16)) for _ in range(3))
+    k2 += 3.0
+    _, lse2 = sage.emulate_rows(q2, k2, v2, np.arange(150), 0.25, 64, return_lse=True)
+    _, ref2 = attention.naive(q2[None, None], k2[None, None], v2[None, None], 0.25)
+    shift = 0.25 * q2 @ sage.k_mean(k2).astype(np.float64)
+    assert np.abs(lse2 + shift - ref2[0, 0]).max() < 0.05
+
+
 def test_key_length_in_emulation():
     rng = np.random.default_rng(7)
     q, k, v = (rng.standard_normal((100, 16)).astype(np.float32) for _ in range(3))

@@ -120,8 +120,12 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// Combine a value with the same lane of the other wave half (lane ^ 32).
 __device__ __forceinline__ float wave_max_halves(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum_halves(float x) {
+  return x + __shfl_xor(x, 32);
 }
 
 }  // namespace fa

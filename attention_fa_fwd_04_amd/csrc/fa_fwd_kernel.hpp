@@ -39,7 +39,7 @@
 
 namespace fa {
 
-template <typename T, int D, int BC, int MASK>
+template <typename T, int D, int BC, int MASK, int NW>
 struct FwdCfg {
   static constexpr int E = Elt<T>::kBytes;
   static constexpr int EPC = 16 / E;              // elements per 16-byte chunk
@@ -52,8 +52,8 @@ struct FwdCfg {
   static constexpr int VBYTES = 32 * PVB * VSTR;
   static constexpr int BUF = KBYTES + VBYTES;
   static constexpr int SB = BC / 32;              // 32-key blocks per tile
-  static constexpr int NT = 256;                  // threads per workgroup
-  static constexpr int BR = 128;                  // query rows per workgroup
+  static constexpr int NT = 64 * NW;              // threads per workgroup
+  static constexpr int BR = 32 * NW;              // query rows per workgroup
   static constexpr int KITEMS = BC * DCH;
   static constexpr int KIT = (KITEMS + NT - 1) / NT;
   static constexpr int VITEMS = (BC / 4) * DCH;
@@ -65,12 +65,12 @@ struct FwdCfg {
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
-template <typename T, int D, int BC, int MASK, int MINB>
-__global__ __launch_bounds__(256, MINB) void fa_fwd_kernel(
+template <typename T, int D, int BC, int MASK, int NW, int MINB>
+__global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, MaskArgs mask,
     int H, int N, int nqt, float c_log2) {
-  using C = FwdCfg<T, D, BC, MASK>;
+  using C = FwdCfg<T, D, BC, MASK, NW>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::BUF];
 
   const int tid = threadIdx.x;
@@ -223,17 +223,28 @@ __global__ __launch_bounds__(256, MINB) void fa_fwd_kernel(
     const uint8_t* vb = kb + C::KBYTES;
     const int kv0 = j * BC;
 
-    // S^T = K Q^T
+    // S^T = K Q^T.  The K operand chunks of 32-key block G + 1 are read while
+    // block G's MFMAs run; the scheduling barriers keep the compiler from
+    // sinking those reads back next to their MFMAs, so LDS latency overlaps
+    // the matrix work.
     f32x16 s[C::SB];
+    u32x4 ka[C::QKS];
+#pragma unroll
+    for (int st = 0; st < C::QKS; ++st)
+      ka[st] = *reinterpret_cast<const u32x4*>(kb + ln * C::KSTR + (2 * st + lh) * 16);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int G = 0; G < C::SB; ++G) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[G][i] = 0.f;
 #pragma unroll
       for (int st = 0; st < C::QKS; ++st) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * G + ln) * C::KSTR + (2 * st + lh) * 16);
+        const u32x4 a = ka[st];
+        if (G + 1 < C::SB)
+          ka[st] = *reinterpret_cast<const u32x4*>(kb + (32 * (G + 1) + ln) * C::KSTR + (2 * st + lh) * 16);
         s[G] = mfma_chunk<T>(a, qreg[st], s[G]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     if constexpr (MASKED) {
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(256, MINB) void fa_fwd_kernel(
   }
 
   // ---- epilogue: O = acc / l, lse = ln 2 * (m + log2 l) ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = wave_sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
     T* orow = O + head_off + (size_t)q_row * D;

@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});
   if (nfull < ntiles) step(nfull, BoolTag<true>{});
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = wave_sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
     T* orow = O + ((size_t)bh * N + q_row) * D;

@@ -11,12 +11,16 @@
 #include "fa_fwd_kernel.hpp"
 #include "fa_int8qk.hpp"
 
-#ifndef FA_FWD_WAVES
-#define FA_FWD_WAVES 8        // waves per workgroup (32 query rows each)
-#endif
-#ifndef FA_FWD_MIN_BLOCKS
-#define FA_FWD_MIN_BLOCKS (8 / FA_FWD_WAVES)   // two waves per SIMD
-#endif
+// Tile configuration per head dimension (measured on MI355X): D = 128 runs
+// 8-wave workgroups (256 query rows) over 128-key tiles; the small head dims
+// run 4-wave workgroups over 64-key tiles; additive masks always use 64-key
+// tiles (per-score mask loads need the registers); fp32 uses 32-key tiles.
+// Every configuration keeps two waves per SIMD.
+template <typename T, int D, int MASK> struct TileCfg {
+  static constexpr int NW = (D >= 128) ? 8 : 4;
+  static constexpr int BC = (sizeof(T) == 4) ? 32 : ((MASK == fa::kMaskAdd || D < 128) ? 64 : 128);
+  static constexpr int MINB = 8 / NW;
+};
 
 namespace {
 
@@ -78,22 +82,14 @@ int check_common(const void* q, const void* k, const void* v, void* o, const flo
 template <typename T, int D, int MASK>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
                int B, int H, int N, float scale, hipStream_t st) {
-#ifndef FA_FWD_BC16
-#define FA_FWD_BC16 128      // keys per tile, 16-bit types
-#endif
-  // keys per tile: the additive-mask path carries per-score mask loads and
-  // keeps 64-key tiles to stay within two waves' registers per SIMD
-  constexpr int BC = (sizeof(T) == 4) ? 32 : (MASK == fa::kMaskAdd ? 64 : FA_FWD_BC16);
-  constexpr int NW = FA_FWD_WAVES;
-  using C = fa::FwdCfg<T, D, BC, MASK, NW>;
+  using TC = TileCfg<T, D, MASK>;
+  using C = fa::FwdCfg<T, D, TC::BC, MASK, TC::NW>;
   const int nqt = (N + C::BR - 1) / C::BR;
   const int grid = B * H * nqt;
   if (log_enabled())
     std::fprintf(stderr, "[fa] fa_fwd dtype=%s D=%d mask=%d B=%d H=%d N=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
-                 sizeof(T) == 4 ? "f32" : "f16/bf16", D, MASK, B, H, N, grid, C::NT, C::BR, BC, 2 * C::BUF);
-  (void)fa::kMaskAdd;
-  constexpr int MINB = FA_FWD_MIN_BLOCKS;
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, BC, MASK, NW, MINB>), dim3(grid), dim3(C::NT), 0, st,
+                 sizeof(T) == 4 ? "f32" : "f16/bf16", D, MASK, B, H, N, grid, C::NT, C::BR, TC::BC, 2 * C::BUF);
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, TC::BC, MASK, TC::NW, TC::MINB>), dim3(grid), dim3(C::NT), 0, st,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                      static_cast<T*>(o), lse, m, H, N, nqt, scale * fa::kLog2e);
   return record_launch("fa_fwd_kernel");

@@ -9,6 +9,7 @@
 
 #include "fa.h"
 #include "fa_fwd_kernel.hpp"
+#include "fa_fwd_dma.hpp"
 #include "fa_int8qk.hpp"
 
 // Tile configuration per head dimension (measured on MI355X): D = 128 runs
@@ -79,20 +80,49 @@ int check_common(const void* q, const void* k, const void* v, void* o, const flo
   return FA_OK;
 }
 
+#ifndef FA_USE_DMA
+#define FA_USE_DMA 1
+#endif
+
 template <typename T, int D, int MASK>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
                int B, int H, int N, float scale, hipStream_t st) {
-  using TC = TileCfg<T, D, MASK>;
-  using C = fa::FwdCfg<T, D, TC::BC, MASK, TC::NW>;
-  const int nqt = (N + C::BR - 1) / C::BR;
-  const int grid = B * H * nqt;
-  if (log_enabled())
-    std::fprintf(stderr, "[fa] fa_fwd dtype=%s D=%d mask=%d B=%d H=%d N=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
-                 sizeof(T) == 4 ? "f32" : "f16/bf16", D, MASK, B, H, N, grid, C::NT, C::BR, TC::BC, 2 * C::BUF);
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, TC::BC, MASK, TC::NW, TC::MINB>), dim3(grid), dim3(C::NT), 0, st,
-                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                     static_cast<T*>(o), lse, m, H, N, nqt, scale * fa::kLog2e);
-  return record_launch("fa_fwd_kernel");
+  if constexpr (FA_USE_DMA && D == 128 && sizeof(T) == 2) {
+    // 16-bit, D = 128: K/V staged by LDS DMA, 8 waves x 128-key tiles (measured
+    // best on MI355X among 4/8 waves x 32/64/128 keys)
+#ifndef FA_DMA_NW
+#define FA_DMA_NW 8
+#endif
+#ifndef FA_DMA_BC
+#define FA_DMA_BC 128
+#endif
+#ifndef FA_DMA_MINB
+#define FA_DMA_MINB (8 / FA_DMA_NW)
+#endif
+    constexpr int NW = FA_DMA_NW, BC = FA_DMA_BC, MINB = FA_DMA_MINB;
+    using C = fa::DmaCfg<T, BC, NW>;
+    const int nqt = (N + C::BR - 1) / C::BR;
+    const int grid = B * H * nqt;
+    if (log_enabled())
+      std::fprintf(stderr, "[fa] fa_fwd(dma) D=%d mask=%d B=%d H=%d N=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
+                   D, MASK, B, H, N, grid, C::NT, C::BR, BC, 4 * C::TILE);
+    hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<T, BC, MASK, NW, MINB>), dim3(grid), dim3(C::NT), 0, st,
+                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                       static_cast<T*>(o), lse, m, H, N, nqt, scale * fa::kLog2e);
+    return record_launch("fa_fwd_dma_kernel");
+  } else {
+    using TC = TileCfg<T, D, MASK>;
+    using C = fa::FwdCfg<T, D, TC::BC, MASK, TC::NW>;
+    const int nqt = (N + C::BR - 1) / C::BR;
+    const int grid = B * H * nqt;
+    if (log_enabled())
+      std::fprintf(stderr, "[fa] fa_fwd dtype=%s D=%d mask=%d B=%d H=%d N=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
+                   sizeof(T) == 4 ? "f32" : "f16/bf16", D, MASK, B, H, N, grid, C::NT, C::BR, TC::BC, 2 * C::BUF);
+    hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, TC::BC, MASK, TC::NW, TC::MINB>), dim3(grid), dim3(C::NT), 0, st,
+                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                       static_cast<T*>(o), lse, m, H, N, nqt, scale * fa::kLog2e);
+    return record_launch("fa_fwd_kernel");
+  }
 }
 
 template <typename T, int D>

@@ -325,21 +325,33 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
                                                       __builtin_bit_cast(i32x4, qreg[st]), si[G], 0, 0, 0);
       }
     }
+    // Full tiles: the row max is taken on the exact int32 sums and scaled once
+    // (the tile's scale c is >= 0), and the scale is folded into the exp2 FMA.
+    // The ragged last tile scales first so dropped keys can be -inf.
     float s[32];
+    float mx;
+    if constexpr (MASKED) {
 #pragma unroll
-    for (int G = 0; G < 2; ++G)
+      for (int G = 0; G < 2; ++G)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float t = (float)si[G][i] * c;
-        if constexpr (MASKED) {
+        for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if (key >= n_eff) t = -INFINITY;
+          s[16 * G + i] = key < n_eff ? (float)si[G][i] * c : -INFINITY;
         }
-        s[16 * G + i] = t;
-      }
-    float mx = -INFINITY;
+      mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) mx = fmaxf(mx, s[i]);
+      for (int i = 0; i < 32; ++i) mx = fmaxf(mx, s[i]);
+    } else {
+      int imx = si[0][0];
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          imx = max(imx, si[G][i]);
+          s[16 * G + i] = (float)si[G][i];
+        }
+      mx = (float)imx * c;
+    }
     mx = wave_max_halves(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -354,14 +366,17 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     }
     // 448 P = exp2(s - m + log2 448) <= 448; the FP8 operand is its e4m3 rounding
     const float moff = m_use - kLog2_448;
+    auto pexp = [&](float x) {
+      return MASKED ? __builtin_amdgcn_exp2f(x - moff) : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -moff));
+    };
     float psum = 0.f;
     uint32_t pk[8];
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
-      const float p0 = __builtin_amdgcn_exp2f(s[i] - moff);
-      const float p1 = __builtin_amdgcn_exp2f(s[i + 1] - moff);
-      const float p2 = __builtin_amdgcn_exp2f(s[i + 2] - moff);
-      const float p3 = __builtin_amdgcn_exp2f(s[i + 3] - moff);
+      const float p0 = pexp(s[i]);
+      const float p1 = pexp(s[i + 1]);
+      const float p2 = pexp(s[i + 2]);
+      const float p3 = pexp(s[i + 3]);
       psum += (p0 + p1) + (p2 + p3);
       int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);

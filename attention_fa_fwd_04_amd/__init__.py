@@ -23,8 +23,8 @@ FA_MASK_NONE, FA_MASK_ADDITIVE, FA_MASK_KEYLEN = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
 FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
 
-EXPORTED = ("fa_fwd", "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk", "fa_int8qk_kv_block",
-            "fa_status_string", "fa_last_hip_error", "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_cross", "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk", "fa_merge",
+            "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
 
 class FAUnavailable(RuntimeError):
@@ -64,10 +64,14 @@ def lib() -> ctypes.CDLL:
     mp = ctypes.POINTER(fa_mask_t)
     h.fa_fwd.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp]
     h.fa_fwd.restype = i32
+    h.fa_fwd_cross.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, i32, f32, i32, vp]
+    h.fa_fwd_cross.restype = i32
     h.fa_fwd_int8qk_workspace_bytes.argtypes = [i32, i32, i32, i32]
     h.fa_fwd_int8qk_workspace_bytes.restype = sz
     h.fa_fwd_int8qk.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     h.fa_fwd_int8qk.restype = i32
+    h.fa_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    h.fa_merge.restype = i32
     h.fa_int8qk_kv_block.argtypes = []
     h.fa_int8qk_kv_block.restype = i32
     h.fa_status_string.argtypes = [i32]
@@ -86,6 +90,10 @@ def fa_fwd(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream) -> int:
     return lib().fa_fwd(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream)
 
 
+def fa_fwd_cross(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, hip_stream) -> int:
+    return lib().fa_fwd_cross(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, hip_stream)
+
+
 def fa_fwd_int8qk_workspace_bytes(B, H, N, D) -> int:
     return lib().fa_fwd_int8qk_workspace_bytes(B, H, N, D)
 
@@ -94,6 +102,10 @@ def fa_fwd_int8qk(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace,
                   workspace_bytes, hip_stream) -> int:
     return lib().fa_fwd_int8qk(q, k, v, o, lse, mask, B, H, N, D, scale, dtype,
                                workspace, workspace_bytes, hip_stream)
+
+
+def fa_merge(o_a, lse_a, o_b, lse_b, o, lse, B, H, N, D, dtype, hip_stream) -> int:
+    return lib().fa_merge(o_a, lse_a, o_b, lse_b, o, lse, B, H, N, D, dtype, hip_stream)
 
 
 def fa_int8qk_kv_block() -> int:
@@ -126,7 +138,7 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def _check_qkv(q, k, v):
+def _check_qkv(q, k, v, same_length=True):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D [B, H, N, D], got {tuple(t.shape)}")
@@ -134,17 +146,22 @@ def _check_qkv(q, k, v):
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [B, H, N, D]")
-    if not (q.shape == k.shape == v.shape):
+    if k.shape != v.shape:
+        raise ValueError(f"k, v shapes differ: {tuple(k.shape)} {tuple(v.shape)}")
+    if q.shape[0] != k.shape[0] or q.shape[1] != k.shape[1] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q and k must share B, H, D: {tuple(q.shape)} {tuple(k.shape)}")
+    if same_length and q.shape != k.shape:
         raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v dtypes differ")
 
 
-def _mask_struct(q, attn_mask, key_len, keep):
+def _mask_struct(q, attn_mask, key_len, keep, nk=None):
     """Build fa_mask_t from a torch mask.  Boolean masks follow the convention
     that False / 0 drops a key and become additive 0 / -inf float32."""
     import torch
     B, H, N, _ = q.shape
+    Nk = N if nk is None else nk
     if attn_mask is not None and key_len is not None:
         raise ValueError("give either attn_mask or key_len, not both")
     if key_len is not None:
@@ -160,7 +177,7 @@ def _mask_struct(q, attn_mask, key_len, keep):
         m = m.to(device=q.device, dtype=torch.float32)
         while m.dim() < 4:
             m = m.unsqueeze(0)
-        m = m.expand(B, H, N, N)
+        m = m.expand(B, H, N, Nk)
         strides = [s if sz > 1 else 0 for s, sz in zip(m.stride(), m.shape)]
         keep.append(m)
         return fa_mask_t(FA_MASK_ADDITIVE, m.data_ptr(), *strides)
@@ -169,22 +186,30 @@ def _mask_struct(q, attn_mask, key_len, keep):
 
 def fwd(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
         return_lse: bool = False, out=None):
-    """O = softmax(scale * q k^T + mask) v for GPU tensors [B, H, N, D]."""
+    """O = softmax(scale * q k^T + mask) v for GPU tensors q [B, H, Nq, D] and
+    k, v [B, H, Nk, D] (self-attention when Nq == Nk, else cross-attention)."""
     import torch
-    _check_qkv(q, k, v)
-    B, H, N, D = q.shape
+    _check_qkv(q, k, v, same_length=False)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if return_lse else None
     keep = []
-    m = _mask_struct(q, attn_mask, key_len, keep)
+    m = _mask_struct(q, attn_mask, key_len, keep, nk=Nk)
     st = torch.cuda.current_stream(q.device).cuda_stream
-    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                lse.data_ptr() if lse is not None else None,
-                ctypes.byref(m) if m is not None else None,
-                B, H, N, D, scale, _dtype_code(q), st)
+    mp = ctypes.byref(m) if m is not None else None
+    lp = lse.data_ptr() if lse is not None else None
+    if Nq == Nk:
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lp, mp,
+                    B, H, Nq, D, scale, _dtype_code(q), st)
+        where = "fa_fwd"
+    else:
+        rc = fa_fwd_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lp, mp,
+                          B, H, Nq, Nk, D, scale, _dtype_code(q), st)
+        where = "fa_fwd_cross"
     if rc != FA_OK:
-        raise FAError(rc, "fa_fwd")
+        raise FAError(rc, where)
     return (o, lse) if return_lse else o
 
 
@@ -209,3 +234,27 @@ def fwd_int8qk(q, k, v, *, key_len=None, scale: Optional[float] = None,
     if rc != FA_OK:
         raise FAError(rc, "fa_fwd_int8qk")
     return (o, lse) if return_lse else o
+
+
+def merge(o_a, lse_a, o_b, lse_b, *, out=None, out_lse=None):
+    """Combine two results over disjoint key sets of the same queries:
+    O [B, H, N, D] and lse [B, H, N] per part; returns (O, lse).  out / out_lse
+    may be o_a / lse_a to accumulate in place."""
+    import torch
+    for t in (o_a, o_b):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("partial outputs must be contiguous 4-D GPU tensors")
+    if o_a.shape != o_b.shape or o_a.dtype != o_b.dtype:
+        raise ValueError("partial outputs differ in shape or dtype")
+    B, H, N, D = o_a.shape
+    for t in (lse_a, lse_b):
+        if t.shape != (B, H, N) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("lse must be contiguous float32 [B, H, N]")
+    o = torch.empty_like(o_a) if out is None else out
+    lse = torch.empty_like(lse_a) if out_lse is None else out_lse
+    st = torch.cuda.current_stream(o_a.device).cuda_stream
+    rc = fa_merge(o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(), o.data_ptr(),
+                  lse.data_ptr(), B, H, N, D, _dtype_code(o_a), st)
+    if rc != FA_OK:
+        raise FAError(rc, "fa_merge")
+    return o, lse

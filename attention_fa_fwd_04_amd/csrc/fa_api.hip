@@ -11,6 +11,7 @@
 #include "fa_fwd_kernel.hpp"
 #include "fa_fwd_dma.hpp"
 #include "fa_int8qk.hpp"
+#include "fa_merge.hpp"
 
 // Tile configuration per head dimension (measured on MI355X): D = 128 runs
 // 8-wave workgroups (256 query rows) over 128-key tiles; the small head dims
@@ -86,7 +87,7 @@ int check_common(const void* q, const void* k, const void* v, void* o, const flo
 
 template <typename T, int D, int MASK>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
-               int B, int H, int N, float scale, hipStream_t st) {
+               int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
   if constexpr (FA_USE_DMA && D == 128 && sizeof(T) == 2) {
     // 16-bit, D = 128: K/V staged by LDS DMA, 8 waves x 128-key tiles (measured
     // best on MI355X among 4/8 waves x 32/64/128 keys)
@@ -101,61 +102,61 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 #endif
     constexpr int NW = FA_DMA_NW, BC = FA_DMA_BC, MINB = FA_DMA_MINB;
     using C = fa::DmaCfg<T, BC, NW>;
-    const int nqt = (N + C::BR - 1) / C::BR;
+    const int nqt = (Nq + C::BR - 1) / C::BR;
     const int grid = B * H * nqt;
     if (log_enabled())
-      std::fprintf(stderr, "[fa] fa_fwd(dma) D=%d mask=%d B=%d H=%d N=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
-                   D, MASK, B, H, N, grid, C::NT, C::BR, BC, 4 * C::TILE);
+      std::fprintf(stderr, "[fa] fa_fwd(dma) D=%d mask=%d B=%d H=%d Nq=%d Nk=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
+                   D, MASK, B, H, Nq, Nk, grid, C::NT, C::BR, BC, 4 * C::TILE);
     hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<T, BC, MASK, NW, MINB>), dim3(grid), dim3(C::NT), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                       static_cast<T*>(o), lse, m, H, N, nqt, scale * fa::kLog2e);
+                       static_cast<T*>(o), lse, m, H, Nq, Nk, nqt, scale * fa::kLog2e);
     return record_launch("fa_fwd_dma_kernel");
   } else {
     using TC = TileCfg<T, D, MASK>;
     using C = fa::FwdCfg<T, D, TC::BC, MASK, TC::NW>;
-    const int nqt = (N + C::BR - 1) / C::BR;
+    const int nqt = (Nq + C::BR - 1) / C::BR;
     const int grid = B * H * nqt;
     if (log_enabled())
-      std::fprintf(stderr, "[fa] fa_fwd dtype=%s D=%d mask=%d B=%d H=%d N=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
-                   sizeof(T) == 4 ? "f32" : "f16/bf16", D, MASK, B, H, N, grid, C::NT, C::BR, TC::BC, 2 * C::BUF);
+      std::fprintf(stderr, "[fa] fa_fwd dtype=%s D=%d mask=%d B=%d H=%d Nq=%d Nk=%d grid=%d block=%d BR=%d BC=%d lds=%d\n",
+                   sizeof(T) == 4 ? "f32" : "f16/bf16", D, MASK, B, H, Nq, Nk, grid, C::NT, C::BR, TC::BC, 2 * C::BUF);
     hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, TC::BC, MASK, TC::NW, TC::MINB>), dim3(grid), dim3(C::NT), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                       static_cast<T*>(o), lse, m, H, N, nqt, scale * fa::kLog2e);
+                       static_cast<T*>(o), lse, m, H, Nq, Nk, nqt, scale * fa::kLog2e);
     return record_launch("fa_fwd_kernel");
   }
 }
 
 template <typename T, int D>
 int dispatch_mask(int kind, const void* q, const void* k, const void* v, void* o, float* lse,
-                  fa::MaskArgs m, int B, int H, int N, float scale, hipStream_t st) {
+                  fa::MaskArgs m, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
   switch (kind) {
-    case FA_MASK_NONE: return launch_fwd<T, D, fa::kMaskNone>(q, k, v, o, lse, m, B, H, N, scale, st);
-    case FA_MASK_ADDITIVE: return launch_fwd<T, D, fa::kMaskAdd>(q, k, v, o, lse, m, B, H, N, scale, st);
-    case FA_MASK_KEYLEN: return launch_fwd<T, D, fa::kMaskLen>(q, k, v, o, lse, m, B, H, N, scale, st);
+    case FA_MASK_NONE: return launch_fwd<T, D, fa::kMaskNone>(q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
+    case FA_MASK_ADDITIVE: return launch_fwd<T, D, fa::kMaskAdd>(q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
+    case FA_MASK_KEYLEN: return launch_fwd<T, D, fa::kMaskLen>(q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
     default: return FA_ERR_ARG;
   }
 }
 
 template <typename T>
 int dispatch_d(int D, int kind, const void* q, const void* k, const void* v, void* o, float* lse,
-               fa::MaskArgs m, int B, int H, int N, float scale, hipStream_t st) {
+               fa::MaskArgs m, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
   switch (D) {
-    case 32: return dispatch_mask<T, 32>(kind, q, k, v, o, lse, m, B, H, N, scale, st);
-    case 40: return dispatch_mask<T, 40>(kind, q, k, v, o, lse, m, B, H, N, scale, st);
-    case 128: return dispatch_mask<T, 128>(kind, q, k, v, o, lse, m, B, H, N, scale, st);
+    case 32: return dispatch_mask<T, 32>(kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
+    case 40: return dispatch_mask<T, 40>(kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
+    case 128: return dispatch_mask<T, 128>(kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
     default: return FA_ERR_UNSUPPORTED;
   }
 }
 
 }  // namespace
 
-extern "C" {
-
-FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-           const fa_mask_t* mask, int B, int H, int N, int D, float scale,
-           fa_dtype_t dtype, void* hip_stream) {
-  int rc = check_common(q, k, v, o, lse, mask, B, H, N, D, scale);
+namespace {
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
+               const fa_mask_t* mask, int B, int H, int Nq, int Nk, int D, float scale,
+               fa_dtype_t dtype, void* hip_stream) {
+  int rc = check_common(q, k, v, o, lse, mask, B, H, Nq, D, scale);
   if (rc != FA_OK) return rc;
+  if (Nk <= 0 || (int64_t)B * H * (int64_t)Nk > (int64_t)1 << 40) return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (D != 32 && D != 40 && D != 128) return FA_ERR_UNSUPPORTED;
   const int kind = mask ? mask->kind : FA_MASK_NONE;
@@ -163,11 +164,26 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (kind != FA_MASK_NONE) m = fa::MaskArgs{mask->ptr, mask->stride_b, mask->stride_h, mask->stride_q, mask->stride_k};
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   switch (dtype) {
-    case FA_F32: return dispatch_d<float>(D, kind, q, k, v, o, lse, m, B, H, N, scale, st);
-    case FA_F16: return dispatch_d<_Float16>(D, kind, q, k, v, o, lse, m, B, H, N, scale, st);
-    case FA_BF16: return dispatch_d<__bf16>(D, kind, q, k, v, o, lse, m, B, H, N, scale, st);
+    case FA_F32: return dispatch_d<float>(D, kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
+    case FA_F16: return dispatch_d<_Float16>(D, kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
+    case FA_BF16: return dispatch_d<__bf16>(D, kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
     default: return FA_ERR_UNSUPPORTED;
   }
+}
+}  // namespace
+
+extern "C" {
+
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+           fa_dtype_t dtype, void* hip_stream) {
+  return fwd_common(q, k, v, o, lse, mask, B, H, N, N, D, scale, dtype, hip_stream);
+}
+
+FA_API int fa_fwd_cross(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const fa_mask_t* mask, int B, int H, int Nq, int Nk, int D, float scale,
+                        fa_dtype_t dtype, void* hip_stream) {
+  return fwd_common(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, hip_stream);
 }
 
 FA_API size_t fa_fwd_int8qk_workspace_bytes(int B, int H, int N, int D) {
@@ -200,6 +216,45 @@ FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, f
     rc = fa::launch_int8qk<_Float16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
   if (rc != FA_OK) return rc;
   return record_launch("fa_fwd_int8qk");
+}
+
+FA_API int fa_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    void* o, float* lse, int B, int H, int N, int D, fa_dtype_t dtype,
+                    void* hip_stream) {
+  if (!o_a || !lse_a || !o_b || !lse_b || !o) return FA_ERR_NULL;
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  const int elt = dtype == FA_F32 ? 4 : 2;
+  if ((D * elt) % 16 != 0 || D * elt > 64 * 16) return FA_ERR_UNSUPPORTED;
+  if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(o, 16)) return FA_ERR_ALIGN;
+  if (!aligned(lse_a, 4) || !aligned(lse_b, 4) || (lse && !aligned(lse, 4))) return FA_ERR_ALIGN;
+  const int64_t rows = (int64_t)B * H * N;
+  if (rows > (int64_t)1 << 40) return FA_ERR_SHAPE;
+  const int cpr = D * elt / 16;
+  int lpr = 1;
+  while (lpr < cpr) lpr *= 2;
+  const int64_t threads = rows * lpr;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > INT32_MAX) return FA_ERR_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  switch (dtype) {
+    case FA_F32:
+      hipLaunchKernelGGL((fa::fa_merge_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         static_cast<const float*>(o_a), lse_a, static_cast<const float*>(o_b), lse_b,
+                         static_cast<float*>(o), lse, rows, D * elt, cpr, lpr);
+      break;
+    case FA_F16:
+      hipLaunchKernelGGL((fa::fa_merge_kernel<_Float16>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         static_cast<const _Float16*>(o_a), lse_a, static_cast<const _Float16*>(o_b), lse_b,
+                         static_cast<_Float16*>(o), lse, rows, D * elt, cpr, lpr);
+      break;
+    default:
+      hipLaunchKernelGGL((fa::fa_merge_kernel<__bf16>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         static_cast<const __bf16*>(o_a), lse_a, static_cast<const __bf16*>(o_b), lse_b,
+                         static_cast<__bf16*>(o), lse, rows, D * elt, cpr, lpr);
+      break;
+  }
+  return record_launch("fa_merge_kernel");
 }
 
 FA_API int fa_int8qk_kv_block(void) { return fa::kInt8Bc; }

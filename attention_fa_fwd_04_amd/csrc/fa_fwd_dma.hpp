@@ -60,7 +60,7 @@ template <typename T, int BC, int MASK, int NW, int MINB>
 __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, MaskArgs mask,
-    int H, int N, int nqt, float c_log2) {
+    int H, int Nq, int Nk, int nqt, float c_log2) {
   using C = DmaCfg<T, BC, NW>;
   constexpr int D = C::D;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];   // K0 K1 V0 V1
@@ -72,21 +72,22 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt, qt = logical - bh * nqt;
   const int b = bh / H, h = bh - b * H;
-  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const size_t q_off = (size_t)bh * (size_t)Nq * D;     // q, o rows
+  const size_t kv_off = (size_t)bh * (size_t)Nk * D;    // k, v rows
   constexpr uint32_t kRow = D * 2;
 
-  int n_eff = N;
+  int n_eff = Nk;
   if constexpr (MASK == kMaskLen) {
     const int L = reinterpret_cast<const int*>(mask.ptr)[b];
-    n_eff = L < 0 ? 0 : (L > N ? N : L);
+    n_eff = L < 0 ? 0 : (L > Nk ? Nk : L);
   }
   const int ntiles = (n_eff + BC - 1) / BC;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head_off, (uint32_t)N * kRow);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head_off, (uint32_t)n_eff * kRow);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head_off, (uint32_t)n_eff * kRow);
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + q_off, (uint32_t)Nq * kRow);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + kv_off, (uint32_t)n_eff * kRow);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + kv_off, (uint32_t)n_eff * kRow);
 
   const int q_row = qt * C::BR + wave * 32 + ln;
-  const bool q_ok = q_row < N;
+  const bool q_ok = q_row < Nq;
   u32x4 qreg[C::QKS];
 #pragma unroll
   for (int s = 0; s < C::QKS; ++s)
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
           float t = -INFINITY;
           if constexpr (kPre) {
-            if (key < N) {
+            if (key < Nk) {
               const float mv = q_ok ? mrow[(int64_t)key * mask.sk] : 0.f;
               t = __builtin_fmaf(s[G][i], c_log2, mv * kLog2e);
             }
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
   const float l_tot = wave_sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
-    T* orow = O + head_off + (size_t)q_row * D;
+    T* orow = O + q_off + (size_t)q_row * D;
 #pragma unroll
     for (int p = 0; p < C::PVB; ++p)
 #pragma unroll
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
                   acc[p][4 * g + 2] * inv, acc[p][4 * g + 3] * inv);
       }
     if (LSE != nullptr && lh == 0)
-      LSE[(size_t)bh * N + q_row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      LSE[(size_t)bh * Nq + q_row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 

@@ -88,6 +88,19 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
            fa_dtype_t dtype, void* hip_stream);
 
 /*
+ * Cross-attention: queries and keys/values of different lengths, as in the
+ * CrossAttention layers the case-study page (section 3.1) routes through the
+ * fused kernel next to SelfAttention (UNet latents attending to text tokens).
+ *   q, o [B,H,Nq,D]; k, v [B,H,Nk,D]; lse [B,H,Nq] or NULL.
+ *   Additive mask element (b,h,i,j) for i < Nq, j < Nk (same strides as
+ *   fa_fwd); a key-length mask counts keys, clamped to [0, Nk].
+ * Everything else as fa_fwd; fa_fwd(.., N, ..) is fa_fwd_cross(.., N, N, ..).
+ */
+FA_API int fa_fwd_cross(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const fa_mask_t* mask, int B, int H, int Nq, int Nk, int D, float scale,
+                        fa_dtype_t dtype, void* hip_stream);
+
+/*
  * INT8-QK / FP8-PV variant (handbook page, section "SageAttention").  Steps:
  *   1. kmean[b,h,:] = token mean of K (float32);
  *   2. Q and K - kmean to INT8, one float32 scale per (b, h, 64-token block),
@@ -128,6 +141,23 @@ FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, f
                   const fa_mask_t* mask, int B, int H, int N, int D, float scale,
                   fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                   void* hip_stream);
+
+/*
+ * Merge two attention results computed for the same queries over disjoint
+ * key sets (K/V split along the sequence, as in ring attention: essay page,
+ * section 6.2):
+ *     lse = log(e^lse_a + e^lse_b),  O = O_a e^(lse_a - lse) + O_b e^(lse_b - lse)
+ * in fp32, rounded to dtype.  A row empty on both sides (lse -inf) gives
+ * O = 0, lse = -inf.
+ *   o_a, o_b, o  [B,H,N,D] dtype;  lse_a, lse_b [B,H,N] float32 (as written
+ *   by fa_fwd / fa_fwd_cross);  lse [B,H,N] float32 or NULL.
+ * o may be o_a and lse may be lse_a (in-place accumulation); other overlaps
+ * are not allowed.  D * sizeof(dtype) must be a multiple of 16 and at most
+ * 1024 bytes.
+ */
+FA_API int fa_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    void* o, float* lse, int B, int H, int N, int D, fa_dtype_t dtype,
+                    void* hip_stream);
 
 /* Keys per tile of the quantised variant's online softmax (P is rounded
  * against the running max, so the result depends on this tile size). */

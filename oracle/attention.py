@@ -163,3 +163,28 @@ def rows(q_rows, k_head, v_head, scale, key_len=None, mask_rows=None, dtype=np.f
     kl = None if key_len is None else np.array([key_len])
     o, lse = naive(q4, k4, v4, scale, m4, kl, dtype)
     return o[0, 0], lse[0, 0]
+
+
+def merge(o_a, lse_a, o_b, lse_b, dtype=np.float64):
+    """Combine two attention results over disjoint key sets of the same queries.
+
+    With lse_x the row log-sum-exp over key set x, the result over the union
+    has lse = log(exp(lse_a) + exp(lse_b)) and O = O_a exp(lse_a - lse) +
+    O_b exp(lse_b - lse): each part's softmax weights are rescaled to the
+    union's denominator, the same rescale the blocked recurrence applies per
+    tile.  Rows empty on both sides give O = 0, lse = -inf.  Shapes
+    O [..., N, D], lse [..., N]."""
+    o_a = np.asarray(o_a, dtype=dtype)
+    o_b = np.asarray(o_b, dtype=dtype)
+    la = np.asarray(lse_a, dtype=dtype)
+    lb = np.asarray(lse_b, dtype=dtype)
+    m = np.maximum(la, lb)
+    dead = ~np.isfinite(m)
+    ref = np.where(dead, 0.0, m)
+    wa, wb = np.exp(la - ref), np.exp(lb - ref)
+    z = wa + wb
+    with np.errstate(invalid="ignore", divide="ignore"):
+        lse = np.where(dead, -np.inf, ref + np.log(z))
+        o = (o_a * wa[..., None] + o_b * wb[..., None]) / z[..., None]
+    o = np.where(dead[..., None], 0.0, o)
+    return o, lse

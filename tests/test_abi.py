@@ -110,3 +110,32 @@ def test_wrapper_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 32)
     with pytest.raises(ValueError):
         fa.fwd(q, q, q)
+
+
+def test_cross_validation(lib):
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, o=P, Nq=100, Nk=77, D=40, dtype=fa.FA_F16, scale=0.1)
+        a.update(kw)
+        return fa.fa_fwd_cross(a["q"], a["k"], a["v"], a["o"], None, None, 2, 8, a["Nq"], a["Nk"], a["D"],
+                               a["scale"], a["dtype"], None)
+    assert call(Nk=0) == fa.FA_ERR_SHAPE
+    assert call(Nq=0) == fa.FA_ERR_SHAPE
+    assert call(v=None) == fa.FA_ERR_NULL
+    assert call(D=64) == fa.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == fa.FA_ERR_ARG
+
+
+def test_merge_validation(lib):
+    def call(**kw):
+        a = dict(oa=P, la=P, ob=P, lb=P, o=P, lse=None, N=10, D=128, dtype=fa.FA_BF16)
+        a.update(kw)
+        return fa.fa_merge(a["oa"], a["la"], a["ob"], a["lb"], a["o"], a["lse"], 1, 2, a["N"], a["D"],
+                           a["dtype"], None)
+    assert call(oa=None) == fa.FA_ERR_NULL
+    assert call(lb=None) == fa.FA_ERR_NULL
+    assert call(N=0) == fa.FA_ERR_SHAPE
+    assert call(D=36) == fa.FA_ERR_UNSUPPORTED          # 72 bytes: not whole 16-byte chunks
+    assert call(D=1024) == fa.FA_ERR_UNSUPPORTED        # rows over 1 KB
+    assert call(dtype=9) == fa.FA_ERR_UNSUPPORTED
+    assert call(o=P + 8) == fa.FA_ERR_ALIGN
+    assert call(lse=P + 2) == fa.FA_ERR_ALIGN

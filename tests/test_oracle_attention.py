@@ -274,3 +274,40 @@ def test_rows_helper_matches_full(qkv):
     orow, lrow = attention.rows(q[1, 2, ids], k[1, 2], v[1, 2], 0.25, key_len=30)
     ofull, _ = attention.naive(q[1:2], k[1:2], v[1:2], 0.25, key_len=np.array([30]))
     assert np.abs(orow - ofull[0, 2, ids]).max() < 1e-14
+
+
+# ---------------------------------------------------------------- merge of key shards
+
+@pytest.mark.parametrize("split", [1, 17, 25, 49])
+def test_merge_of_key_split_equals_full(split):
+    """Attention over keys [0, s) and [s, N) merged by lse equals attention over
+    all keys (sequence sharding of K/V, the essay's ring-attention section)."""
+    q, k, v = (_rand((2, 3, 30, 8), s) for s in (31, 32, 33))
+    k, v = np.concatenate([k, k[:, :, :20]], axis=2), np.concatenate([v, v[:, :, :20]], axis=2)
+    o_full, l_full = attention.naive(q, k, v, 0.4)
+    oa, la = attention.naive(q, k[:, :, :split], v[:, :, :split], 0.4)
+    ob, lb = attention.naive(q, k[:, :, split:], v[:, :, split:], 0.4)
+    o, lse = attention.merge(oa, la, ob, lb)
+    assert np.abs(o - o_full).max() < 1e-13 and np.abs(lse - l_full).max() < 1e-12
+
+
+def test_merge_handles_empty_sides():
+    q, k, v = (_rand((1, 1, 4, 8), s) for s in (34, 35, 36))
+    o1, l1 = attention.naive(q, k, v, 0.3)
+    dead_o, dead_l = np.zeros_like(o1), np.full_like(l1, -np.inf)
+    for o, lse in (attention.merge(o1, l1, dead_o, dead_l), attention.merge(dead_o, dead_l, o1, l1)):
+        assert np.abs(o - o1).max() < 1e-15 and np.abs(lse - l1).max() < 1e-15
+    o, lse = attention.merge(dead_o, dead_l, dead_o, dead_l)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+def test_cross_attention_shapes_in_oracle():
+    """Nq != Nk: the definition against a library routine."""
+    q = _rand((2, 2, 13, 16), 37)
+    k, v = _rand((2, 2, 40, 16), 38), _rand((2, 2, 40, 16), 39)
+    o, _ = attention.naive(q, k, v, 0.25, key_len=np.array([40, 9]))
+    keep = np.arange(40)[None, :] < np.array([40, 9])[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(keep[:, None, None, :]), scale=0.25).numpy()
+    assert np.abs(o - ref).max() < 1e-12

@@ -50,6 +50,12 @@ class Workload:
     k_offset_var: float = 0.0    # per-(b,h,channel) K offset ~ N(0, var)
     quantised: bool = False      # run through the INT8-QK / FP8-PV entry point
     sampled_rows: int = 0        # rows the oracle checks at full size (0 = all)
+    Nk: int = 0                  # key / value length when it differs from N (cross-attention)
+    merge: bool = False          # time the merge of two partial results of this shape
+
+    @property
+    def n_keys(self) -> int:
+        return self.Nk if self.Nk else self.N
 
     @property
     def scale(self) -> float:
@@ -72,6 +78,10 @@ WORKLOADS = {
                 outlier_channels=4, sampled_rows=512),
     5: Workload(5, "wan-720p-int8qk", "bf16", 1, 40, 76112, 128,
                 k_offset_var=2.0, quantised=True, sampled_rows=512),
+    # cross-attention of an SD1.5 768^2 UNet block (4096 latents x 77 text tokens)
+    6: Workload(6, "sd15-text-cross", "f16", 2, 8, 4096, 40, Nk=77),
+    # merge of two partial results of the FLUX-1024^2 layer (key split)
+    7: Workload(7, "flux-1024-merge", "bf16", 1, 24, 4608, 128, merge=True),
 }
 
 
@@ -99,7 +109,7 @@ def key_lengths(w: Workload) -> Optional[np.ndarray]:
 
 def head_f32(w: Workload, tid: int, b: int, h: int) -> np.ndarray:
     """One (b, h) head of q (tid 0), k (1) or v (2) as float32 before rounding."""
-    x = _normal_head(w.wid, tid, b, h, w.N, w.D)
+    x = _normal_head(w.wid, tid, b, h, w.N if tid == T_Q else w.n_keys, w.D)
     if tid == T_K:
         if w.outlier_channels:
             x[:, outlier_channel_ids(w)] *= np.float32(w.outlier_scale)
@@ -126,7 +136,7 @@ def make_inputs(w: Workload, threads: int = 8) -> dict:
         return {"q": q, "k": k, "v": v, "key_len": None}
     out = {}
     for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V)):
-        x = np.empty((w.B, w.H, w.N, w.D), dtype=np.float32)
+        x = np.empty((w.B, w.H, w.N if tid == T_Q else w.n_keys, w.D), dtype=np.float32)
 
         def fill(bh, x=x, tid=tid):
             b, h = divmod(bh, w.H)

@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·D/s) and % of MFMA peak, 1 MI355X"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "int8qk": 5000.0}
+PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "attention_fa_fwd_04_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -78,12 +79,12 @@ def cpu_baseline(w, budget_s: float = 20.0, min_s: float = 10.0) -> dict:
                 break
         if t_total >= budget_s:
             break
-    flops = 4.0 * done * w.N * w.N * w.D
+    flops = 4.0 * done * w.N * w.n_keys * w.D
     cores = len(os.sched_getaffinity(0))
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores,
             "kind": "oracle",
             "sample": f"{done} head evaluations ({passes} pass(es) over the {len(heads)} heads) of {w.name} "
-                      f"(N={w.N}, D={w.D}), numpy float64 naive formula, {t_total:.1f} s, "
+                      f"(N={w.N}, Nk={w.n_keys}, D={w.D}), numpy float64 naive formula, {t_total:.1f} s, "
                       f"BLAS threads {blas_threads}, host cores {cores}"}
 
 
@@ -114,16 +115,7 @@ def main() -> int:
     fa.lib()
     dev = torch.device("cuda", 0)
 
-    def measure(w, steps, warmup):
-        inp = make_inputs(w)
-        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
-        kl = None if inp["key_len"] is None else inp["key_len"].to(dev)
-        o = torch.empty_like(q)
-        if w.quantised:
-            ws = torch.empty(fa.fa_fwd_int8qk_workspace_bytes(w.B, w.H, w.N, w.D), dtype=torch.uint8, device=dev)
-            call = lambda: fa.fwd_int8qk(q, k, v, key_len=kl, workspace=ws, out=o)  # noqa: E731
-        else:
-            call = lambda: fa.fwd(q, k, v, key_len=kl, out=o)  # noqa: E731
+    def timed(call, steps, warmup):
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
@@ -137,9 +129,31 @@ def main() -> int:
         e1.record(st)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ev_ms = e0.elapsed_time(e1) / steps
-        del q, k, v, o
-        return ev_ms, wall / steps * 1e3
+        return e0.elapsed_time(e1) / steps, wall / steps * 1e3
+
+    def measure(w, steps, warmup):
+        if w.merge:
+            # two partial results of the layer (seeded) merged into a third buffer
+            g = torch.Generator(device="cpu").manual_seed(w.wid)
+            shape = (w.B, w.H, w.N, w.D)
+            oa, ob = (torch.randn(shape, generator=g).to(w.torch_dtype).to(dev) for _ in range(2))
+            la, lb = (torch.randn(shape[:3], generator=g).to(dev) for _ in range(2))
+            o, lse = torch.empty_like(oa), torch.empty_like(la)
+            return timed(lambda: fa.merge(oa, la, ob, lb, out=o, out_lse=lse), steps, warmup)
+        inp = make_inputs(w)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        kl = None if inp["key_len"] is None else inp["key_len"].to(dev)
+        o = torch.empty_like(q)
+        if w.quantised:
+            ws = torch.empty(fa.fa_fwd_int8qk_workspace_bytes(w.B, w.H, w.N, w.D), dtype=torch.uint8, device=dev)
+            call = lambda: fa.fwd_int8qk(q, k, v, key_len=kl, workspace=ws, out=o)  # noqa: E731
+        else:
+            call = lambda: fa.fwd(q, k, v, key_len=kl, out=o)  # noqa: E731
+        return timed(call, steps, warmup)
+
+    def merge_bytes(w):
+        elt = 4 if w.dtype == "f32" else 2
+        return 3 * w.B * w.H * w.N * w.D * elt + 3 * w.B * w.H * w.N * 4
 
     if args.copy_calibration_mib:
         # a plain copy of known size: reads and writes exactly this many bytes
@@ -153,12 +167,24 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     ev_ms, wall_ms = measure(w, args.steps, args.warmup)
-    flops = 4.0 * w.B * w.H * w.N * w.N * w.D
+    if w.merge:
+        gbs = merge_bytes(w) / (ev_ms * 1e-3) / 1e9
+        out = {"metric": "lse merge of two partial attention results, GB/s (bytes read + written / s)",
+               "value": round(merge_bytes(w) / (wall_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+               "data": "synthetic (seeded)",
+               "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D},
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for(f"fa_merge:{w.name}")}}
+        print(json.dumps(out), flush=True)
+        return 0
+    flops = 4.0 * w.B * w.H * w.N * w.n_keys * w.D
     tflops_step = flops / (wall_ms * 1e-3) / 1e12
     tflops_kernel = flops / (ev_ms * 1e-3) / 1e12
     dkey = "int8qk" if w.quantised else w.dtype
     peak = PEAK_TFLOPS[dkey]
-    kernel_key = f"{'fa_fwd_int8qk' if w.quantised else 'fa_fwd'}:{w.name}"
+    kernel_key = f"{'fa_fwd_int8qk' if w.quantised else ('fa_fwd_cross' if w.Nk else 'fa_fwd')}:{w.name}"
     out = {
         "metric": METRIC,
         "value": round(tflops_step, 2),
@@ -172,19 +198,32 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "int8/fp8 (bf16 in/out)" if w.quantised else w.dtype,
         "data": "synthetic (seeded N(0,1) tensors of the workload's shape)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "Nk": w.n_keys, "D": w.D,
                    "mask": "key_len" if w.key_len else "none", "causal": False},
         "roofline": {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops_kernel / peak, 4),
                      "traffic": traffic_for(kernel_key)},
     }
+    # Q and O once, K and V once: with few keys (cross-attention on a short
+    # text sequence) moving these bytes takes longer than the MFMA work
+    elt = 4 if w.dtype == "f32" else 2
+    io_bytes = 2.0 * w.B * w.H * (w.N + w.n_keys) * w.D * elt
+    if io_bytes / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12):
+        gbs = io_bytes / (ev_ms * 1e-3) / 1e9
+        out["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     if args.extra:
         extra = {}
-        for wid in (3, 4, 5):
+        for wid in (3, 4, 5, 6, 7):
             wx = WORKLOADS[wid]
-            fl = 4.0 * wx.B * wx.H * wx.N * wx.N * wx.D
+            if wx.merge:
+                e_ms, _ = measure(wx, 50, 3)
+                gb = merge_bytes(wx) / (e_ms * 1e-3) / 1e9
+                extra[wx.name] = {"ms": round(e_ms, 4), "GB/s": round(gb, 1), "hbm_frac": round(gb / PEAK_HBM_GBS, 3)}
+                continue
+            fl = 4.0 * wx.B * wx.H * wx.N * wx.n_keys * wx.D
             try:
                 e_ms, _ = measure(wx, 3 if wid in (4, 5) else 10, 1)
                 extra[wx.name] = {"ms": round(e_ms, 3), "tflops": round(fl / (e_ms * 1e-3) / 1e12, 2)}

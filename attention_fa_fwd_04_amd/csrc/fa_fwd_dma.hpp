@@ -15,7 +15,7 @@
 //    lane that lands at physical chunk c of row r fetches logical chunk
 //    c ^ f(r) from global memory.  K uses f(r) = r & 15, which spreads the
 //    16 rows one ds_read_b128 phase touches over all 16 chunk slots; V uses
-//    f(r) = 2 (r & 7), which does the same for the transposing reads below.
+//    the bit map v_swz below, which does the same for the transposing reads.
 //  * V stays row-major in LDS.  The P V operand needs, per lane, consecutive
 //    keys at one channel; ds_read_b64_tr_b16 provides exactly that: within
 //    each 16-lane group, lane 4k + t fetches 4 channels (4t .. 4t+3) of key
@@ -50,7 +50,12 @@ struct DmaCfg {
 };
 
 __device__ __forceinline__ int k_swz(int r) { return r & 15; }
-__device__ __forceinline__ int v_swz(int r) { return (r & 7) << 1; }
+// V: bits 0, 1, 2 of the row go to chunk bits 3, 2, 1.  The LDS serves a
+// transposing read 32 lanes at a time; lanes 0-31 read 4 consecutive rows,
+// each at two adjacent 32-byte chunk pairs.  Under this map those 8
+// (row, pair) combinations fall in 8 distinct 32-byte bank groups, so the
+// read is conflict-free (the previous map, 2 (r & 7), sent them to 4).
+__device__ __forceinline__ int v_swz(int r) { return ((r & 1) << 3) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));

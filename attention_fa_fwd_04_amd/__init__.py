@@ -23,8 +23,8 @@ FA_MASK_NONE, FA_MASK_ADDITIVE, FA_MASK_KEYLEN = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
 FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
 
-EXPORTED = ("fa_fwd", "fa_fwd_cross", "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk", "fa_merge",
-            "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_cross", "fa_fwd_strided", "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk",
+            "fa_merge", "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
 
 class FAUnavailable(RuntimeError):
@@ -44,6 +44,10 @@ class fa_mask_t(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("ptr", ctypes.c_void_p),
                 ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
                 ("stride_q", ctypes.c_int64), ("stride_k", ctypes.c_int64)]
+
+
+class fa_stride_t(ctypes.Structure):
+    _fields_ = [("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
 
 
 _lib_handle = None
@@ -66,6 +70,9 @@ def lib() -> ctypes.CDLL:
     h.fa_fwd.restype = i32
     h.fa_fwd_cross.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, i32, f32, i32, vp]
     h.fa_fwd_cross.restype = i32
+    sp = ctypes.POINTER(fa_stride_t)
+    h.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, i32, sp, sp, sp, sp, f32, i32, vp]
+    h.fa_fwd_strided.restype = i32
     h.fa_fwd_int8qk_workspace_bytes.argtypes = [i32, i32, i32, i32]
     h.fa_fwd_int8qk_workspace_bytes.restype = sz
     h.fa_fwd_int8qk.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
@@ -92,6 +99,12 @@ def fa_fwd(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream) -> int:
 
 def fa_fwd_cross(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, hip_stream) -> int:
     return lib().fa_fwd_cross(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, hip_stream)
+
+
+def fa_fwd_strided(q, k, v, o, lse, mask, B, H, Nq, Nk, D, q_strides, k_strides, v_strides,
+                   o_strides, scale, dtype, hip_stream) -> int:
+    return lib().fa_fwd_strided(q, k, v, o, lse, mask, B, H, Nq, Nk, D, q_strides, k_strides,
+                                v_strides, o_strides, scale, dtype, hip_stream)
 
 
 def fa_fwd_int8qk_workspace_bytes(B, H, N, D) -> int:
@@ -138,13 +151,16 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def _check_qkv(q, k, v, same_length=True):
+def _check_qkv(q, k, v, same_length=True, strided=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D [B, H, N, D], got {tuple(t.shape)}")
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
+        if strided:
+            if t.stride(3) != 1:
+                raise ValueError(f"{name} must have contiguous D (stride(3) == 1)")
+        elif not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [B, H, N, D]")
     if k.shape != v.shape:
         raise ValueError(f"k, v shapes differ: {tuple(k.shape)} {tuple(v.shape)}")
@@ -187,20 +203,30 @@ def _mask_struct(q, attn_mask, key_len, keep, nk=None):
 def fwd(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
         return_lse: bool = False, out=None):
     """O = softmax(scale * q k^T + mask) v for GPU tensors q [B, H, Nq, D] and
-    k, v [B, H, Nk, D] (self-attention when Nq == Nk, else cross-attention)."""
+    k, v [B, H, Nk, D] (self-attention when Nq == Nk, else cross-attention).
+    The tensors may be strided views with contiguous D (e.g. [B, N, H, D]
+    projections viewed through .transpose(1, 2)); those go through
+    fa_fwd_strided without a copy.  O has q's layout unless `out` is given."""
     import torch
-    _check_qkv(q, k, v, same_length=False)
+    _check_qkv(q, k, v, same_length=False, strided=True)
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or o.stride(3) != 1:
+        raise ValueError("out must match q in shape and dtype, with contiguous D")
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if return_lse else None
     keep = []
     m = _mask_struct(q, attn_mask, key_len, keep, nk=Nk)
     st = torch.cuda.current_stream(q.device).cuda_stream
     mp = ctypes.byref(m) if m is not None else None
     lp = lse.data_ptr() if lse is not None else None
-    if Nq == Nk:
+    if not all(t.is_contiguous() for t in (q, k, v, o)):
+        sd = [fa_stride_t(t.stride(0), t.stride(1), t.stride(2)) for t in (q, k, v, o)]
+        rc = fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lp, mp,
+                            B, H, Nq, Nk, D, *[ctypes.byref(x) for x in sd], scale, _dtype_code(q), st)
+        where = "fa_fwd_strided"
+    elif Nq == Nk:
         rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lp, mp,
                     B, H, Nq, D, scale, _dtype_code(q), st)
         where = "fa_fwd"

@@ -85,9 +85,14 @@ int check_common(const void* q, const void* k, const void* v, void* o, const flo
 #define FA_USE_DMA 1
 #endif
 
+// Row layouts of q, k, v, o in that order.
+struct Layouts {
+  fa::RowLayout q, k, v, o;
+};
+
 template <typename T, int D, int MASK>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
-               int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
+               const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
   if constexpr (FA_USE_DMA && D == 128 && sizeof(T) == 2) {
     // 16-bit, D = 128: K/V staged by LDS DMA, 8 waves x 128-key tiles (measured
     // best on MI355X among 4/8 waves x 32/64/128 keys)
@@ -109,7 +114,7 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    D, MASK, B, H, Nq, Nk, grid, C::NT, C::BR, BC, 4 * C::TILE);
     hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<T, BC, MASK, NW, MINB>), dim3(grid), dim3(C::NT), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                       static_cast<T*>(o), lse, m, H, Nq, Nk, nqt, scale * fa::kLog2e);
+                       static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e);
     return record_launch("fa_fwd_dma_kernel");
   } else {
     using TC = TileCfg<T, D, MASK>;
@@ -121,29 +126,29 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    sizeof(T) == 4 ? "f32" : "f16/bf16", D, MASK, B, H, Nq, Nk, grid, C::NT, C::BR, TC::BC, 2 * C::BUF);
     hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, TC::BC, MASK, TC::NW, TC::MINB>), dim3(grid), dim3(C::NT), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                       static_cast<T*>(o), lse, m, H, Nq, Nk, nqt, scale * fa::kLog2e);
+                       static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e);
     return record_launch("fa_fwd_kernel");
   }
 }
 
 template <typename T, int D>
 int dispatch_mask(int kind, const void* q, const void* k, const void* v, void* o, float* lse,
-                  fa::MaskArgs m, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
+                  fa::MaskArgs m, const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
   switch (kind) {
-    case FA_MASK_NONE: return launch_fwd<T, D, fa::kMaskNone>(q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
-    case FA_MASK_ADDITIVE: return launch_fwd<T, D, fa::kMaskAdd>(q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
-    case FA_MASK_KEYLEN: return launch_fwd<T, D, fa::kMaskLen>(q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
+    case FA_MASK_NONE: return launch_fwd<T, D, fa::kMaskNone>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+    case FA_MASK_ADDITIVE: return launch_fwd<T, D, fa::kMaskAdd>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+    case FA_MASK_KEYLEN: return launch_fwd<T, D, fa::kMaskLen>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
     default: return FA_ERR_ARG;
   }
 }
 
 template <typename T>
 int dispatch_d(int D, int kind, const void* q, const void* k, const void* v, void* o, float* lse,
-               fa::MaskArgs m, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
+               fa::MaskArgs m, const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
   switch (D) {
-    case 32: return dispatch_mask<T, 32>(kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
-    case 40: return dispatch_mask<T, 40>(kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
-    case 128: return dispatch_mask<T, 128>(kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
+    case 32: return dispatch_mask<T, 32>(kind, q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+    case 40: return dispatch_mask<T, 40>(kind, q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+    case 128: return dispatch_mask<T, 128>(kind, q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
     default: return FA_ERR_UNSUPPORTED;
   }
 }
@@ -151,9 +156,33 @@ int dispatch_d(int D, int kind, const void* q, const void* k, const void* v, voi
 }  // namespace
 
 namespace {
+Layouts contiguous_layouts(int H, int Nq, int Nk, int D) {
+  const fa::RowLayout lq{(int64_t)H * Nq * D, (int64_t)Nq * D, D};
+  const fa::RowLayout lk{(int64_t)H * Nk * D, (int64_t)Nk * D, D};
+  return Layouts{lq, lk, lk, lq};
+}
+
+// Kernels form 32-bit byte offsets for rows up to one tile (or one query
+// block) past the last: with this margin those offsets never wrap, so they
+// fall outside the buffer range and read as zero.
+constexpr int64_t kRowMargin = 256;
+
+// A strided view: non-negative strides, 16-byte aligned rows and (b, h)
+// bases, and every row offset within the 32-bit range of a buffer resource.
+int check_layout(const fa_stride_t* s, int rows, int D, size_t elt, bool output) {
+  if (!s) return FA_ERR_NULL;
+  if (s->stride_b < 0 || s->stride_h < 0 || s->stride_n <= 0) return FA_ERR_ARG;
+  if (output && s->stride_n < D) return FA_ERR_ARG;
+  if ((s->stride_b * (int64_t)elt) % 16 || (s->stride_h * (int64_t)elt) % 16 ||
+      (s->stride_n * (int64_t)elt) % 16)
+    return FA_ERR_ALIGN;
+  if ((int64_t)(rows + kRowMargin) * s->stride_n * (int64_t)elt > (int64_t)UINT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
                const fa_mask_t* mask, int B, int H, int Nq, int Nk, int D, float scale,
-               fa_dtype_t dtype, void* hip_stream) {
+               fa_dtype_t dtype, const Layouts& L, void* hip_stream) {
   int rc = check_common(q, k, v, o, lse, mask, B, H, Nq, D, scale);
   if (rc != FA_OK) return rc;
   if (Nk <= 0 || (int64_t)B * H * (int64_t)Nk > (int64_t)1 << 40) return FA_ERR_SHAPE;
@@ -164,11 +193,19 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   if (kind != FA_MASK_NONE) m = fa::MaskArgs{mask->ptr, mask->stride_b, mask->stride_h, mask->stride_q, mask->stride_k};
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   switch (dtype) {
-    case FA_F32: return dispatch_d<float>(D, kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
-    case FA_F16: return dispatch_d<_Float16>(D, kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
-    case FA_BF16: return dispatch_d<__bf16>(D, kind, q, k, v, o, lse, m, B, H, Nq, Nk, scale, st);
+    case FA_F32: return dispatch_d<float>(D, kind, q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+    case FA_F16: return dispatch_d<_Float16>(D, kind, q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+    case FA_BF16: return dispatch_d<__bf16>(D, kind, q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
     default: return FA_ERR_UNSUPPORTED;
   }
+}
+
+size_t dtype_bytes(int dt) { return dt == FA_F32 ? 4 : 2; }
+
+int contiguous_range_ok(int Nq, int Nk, int D, int dt) {
+  const int64_t e = (int64_t)dtype_bytes(dt);
+  return (int64_t)(Nq + kRowMargin) * D * e <= (int64_t)UINT32_MAX &&
+         (int64_t)(Nk + kRowMargin) * D * e <= (int64_t)UINT32_MAX;
 }
 }  // namespace
 
@@ -177,13 +214,33 @@ extern "C" {
 FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const fa_mask_t* mask, int B, int H, int N, int D, float scale,
            fa_dtype_t dtype, void* hip_stream) {
-  return fwd_common(q, k, v, o, lse, mask, B, H, N, N, D, scale, dtype, hip_stream);
+  return fa_fwd_cross(q, k, v, o, lse, mask, B, H, N, N, D, scale, dtype, hip_stream);
 }
 
 FA_API int fa_fwd_cross(const void* q, const void* k, const void* v, void* o, float* lse,
                         const fa_mask_t* mask, int B, int H, int Nq, int Nk, int D, float scale,
                         fa_dtype_t dtype, void* hip_stream) {
-  return fwd_common(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, hip_stream);
+  if (Nq > 0 && Nk > 0 && D > 0 && !contiguous_range_ok(Nq, Nk, D, dtype)) return FA_ERR_SHAPE;
+  return fwd_common(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype,
+                    contiguous_layouts(H, Nq, Nk, D), hip_stream);
+}
+
+FA_API int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const fa_mask_t* mask, int B, int H, int Nq, int Nk, int D,
+                          const fa_stride_t* q_strides, const fa_stride_t* k_strides,
+                          const fa_stride_t* v_strides, const fa_stride_t* o_strides,
+                          float scale, fa_dtype_t dtype, void* hip_stream) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || D <= 0) return FA_ERR_SHAPE;
+  const size_t e = dtype_bytes(dtype);
+  int rc;
+  if ((rc = check_layout(q_strides, Nq, D, e, false)) != FA_OK) return rc;
+  if ((rc = check_layout(k_strides, Nk, D, e, false)) != FA_OK) return rc;
+  if ((rc = check_layout(v_strides, Nk, D, e, false)) != FA_OK) return rc;
+  if ((rc = check_layout(o_strides, Nq, D, e, true)) != FA_OK) return rc;
+  auto rl = [](const fa_stride_t* s) { return fa::RowLayout{s->stride_b, s->stride_h, s->stride_n}; };
+  const Layouts L{rl(q_strides), rl(k_strides), rl(v_strides), rl(o_strides)};
+  return fwd_common(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, L, hip_stream);
 }
 
 FA_API size_t fa_fwd_int8qk_workspace_bytes(int B, int H, int N, int D) {

@@ -30,6 +30,12 @@ struct MaskArgs {
   int64_t sb, sh, sq, sk;
 };
 
+// Element strides of a [B, H, N, D] tensor whose D elements are contiguous:
+// element (b, h, n, d) is at base[b * sb + h * sh + n * sn + d].
+struct RowLayout {
+  int64_t sb, sh, sn;
+};
+
 template <typename T> struct Elt;
 template <> struct Elt<float>    { static constexpr int kBytes = 4; };
 template <> struct Elt<_Float16> { static constexpr int kBytes = 2; };

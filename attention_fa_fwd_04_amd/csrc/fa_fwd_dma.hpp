@@ -65,6 +65,7 @@ template <typename T, int BC, int MASK, int NW, int MINB>
 __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, MaskArgs mask,
+    RowLayout lq, RowLayout lk, RowLayout lv, RowLayout lo,
     int H, int Nq, int Nk, int nqt, float c_log2) {
   using C = DmaCfg<T, BC, NW>;
   constexpr int D = C::D;
@@ -77,9 +78,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt, qt = logical - bh * nqt;
   const int b = bh / H, h = bh - b * H;
-  const size_t q_off = (size_t)bh * (size_t)Nq * D;     // q, o rows
-  const size_t kv_off = (size_t)bh * (size_t)Nk * D;    // k, v rows
-  constexpr uint32_t kRow = D * 2;
+  // Row pitches in bytes (D contiguous; validated to fit the 32-bit ranges).
+  const uint32_t qs = (uint32_t)(lq.sn * 2), ks = (uint32_t)(lk.sn * 2), vs = (uint32_t)(lv.sn * 2);
 
   int n_eff = Nk;
   if constexpr (MASK == kMaskLen) {
@@ -87,16 +87,16 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
     n_eff = L < 0 ? 0 : (L > Nk ? Nk : L);
   }
   const int ntiles = (n_eff + BC - 1) / BC;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + q_off, (uint32_t)Nq * kRow);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + kv_off, (uint32_t)n_eff * kRow);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + kv_off, (uint32_t)n_eff * kRow);
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + b * lq.sb + h * lq.sh, (uint32_t)Nq * qs);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + b * lk.sb + h * lk.sh, (uint32_t)n_eff * ks);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + b * lv.sb + h * lv.sh, (uint32_t)n_eff * vs);
 
   const int q_row = qt * C::BR + wave * 32 + ln;
   const bool q_ok = q_row < Nq;
   u32x4 qreg[C::QKS];
 #pragma unroll
   for (int s = 0; s < C::QKS; ++s)
-    qreg[s] = buf_load16(qr, (uint32_t)q_row * kRow + (2 * s + lh) * 16);
+    qreg[s] = buf_load16(qr, (uint32_t)q_row * qs + (2 * s + lh) * 16);
 
   // Rows the DMA never reaches (past n_eff) must hold finite values: clear
   // both V buffers once.
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
   // kilobyte (wave * DMA_PER_WAVE + i): rows 4 per kilobyte, this lane's
   // 16 bytes at row r, physical chunk lane % 16.
   auto dma_tile = [&](int j) {
-    const uint32_t base = (uint32_t)(j * BC) * kRow;
+    const uint32_t row0 = (uint32_t)(j * BC);
     uint8_t* kb = smem + (j & 1) * C::TILE;
     uint8_t* vb = smem + 2 * C::TILE + (j & 1) * C::TILE;
 #pragma unroll
@@ -116,8 +116,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
       const int kb_idx = wave * C::DMA_PER_WAVE + i;
       const int r = kb_idx * 4 + (lane >> 4);
       const int pc = lane & 15;
-      const uint32_t koff = base + (uint32_t)r * kRow + ((pc ^ k_swz(r)) << 4);
-      const uint32_t voff = base + (uint32_t)r * kRow + ((pc ^ v_swz(r)) << 4);
+      const uint32_t koff = (row0 + r) * ks + ((pc ^ k_swz(r)) << 4);
+      const uint32_t voff = (row0 + r) * vs + ((pc ^ v_swz(r)) << 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kb + kb_idx * 1024), 16, koff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vb + kb_idx * 1024), 16, voff, 0, 0, 0);
     }
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
   const float l_tot = wave_sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
-    T* orow = O + q_off + (size_t)q_row * D;
+    T* orow = O + b * lo.sb + h * lo.sh + (int64_t)q_row * lo.sn;
 #pragma unroll
     for (int p = 0; p < C::PVB; ++p)
 #pragma unroll

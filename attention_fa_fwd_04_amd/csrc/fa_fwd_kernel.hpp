@@ -69,6 +69,7 @@ template <typename T, int D, int BC, int MASK, int NW, int MINB>
 __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, MaskArgs mask,
+    RowLayout lq, RowLayout lk, RowLayout lv, RowLayout lo,
     int H, int Nq, int Nk, int nqt, float c_log2) {
   using C = FwdCfg<T, D, BC, MASK, NW>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::BUF];
@@ -80,9 +81,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt, qt = logical - bh * nqt;
   const int b = bh / H, h = bh - b * H;
-  const size_t q_off = (size_t)bh * (size_t)Nq * D;     // q, o rows
-  const size_t kv_off = (size_t)bh * (size_t)Nk * D;    // k, v rows
-  constexpr uint32_t kRow = D * C::E;             // bytes per row
+  // Row pitches in bytes (D contiguous; validated to fit the 32-bit ranges).
+  const uint32_t qs = (uint32_t)(lq.sn * C::E), ks = (uint32_t)(lk.sn * C::E), vs = (uint32_t)(lv.sn * C::E);
 
   int n_eff = Nk;
   if constexpr (MASK == kMaskLen) {
@@ -91,9 +91,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
   }
   const int ntiles = (n_eff + BC - 1) / BC;
   // Rows at or past n_eff read as zero: K and V ranges end there.
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + q_off, (uint32_t)Nq * kRow);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + kv_off, (uint32_t)n_eff * kRow);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + kv_off, (uint32_t)n_eff * kRow);
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + b * lq.sb + h * lq.sh, (uint32_t)Nq * qs);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + b * lk.sb + h * lk.sh, (uint32_t)n_eff * ks);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + b * lv.sb + h * lv.sh, (uint32_t)n_eff * vs);
 
   const int q_row = qt * C::BR + wave * 32 + ln;
   const bool q_ok = q_row < Nq;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
 #pragma unroll
   for (int s = 0; s < C::QKS; ++s) {
     const int ch = 2 * s + lh;
-    qreg[s] = buf_load16(qr, ch < C::DCH ? (uint32_t)q_row * kRow + ch * 16 : kOobOffset);
+    qreg[s] = buf_load16(qr, ch < C::DCH ? (uint32_t)q_row * qs + ch * 16 : kOobOffset);
   }
 
   // Zero the padding the tile writes never touch: K chunks past D (QK steps
@@ -133,11 +133,12 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
   // Loads past the last tile read zeros (outside the buffer range), so the
   // prefetch needs no guard.
   auto load_tile = [&](int j) {
-    const uint32_t base = (uint32_t)(j * BC) * kRow;
+    const uint32_t row0 = (uint32_t)(j * BC);
 #pragma unroll
     for (int i = 0; i < C::KIT; ++i) {
       const int it = tid + i * C::NT;
-      kst[i] = buf_load16(kr, (C::KITEMS % C::NT == 0 || it < C::KITEMS) ? base + it * 16 : kOobOffset);
+      const uint32_t row = row0 + it / C::DCH, c = it % C::DCH;
+      kst[i] = buf_load16(kr, (C::KITEMS % C::NT == 0 || it < C::KITEMS) ? row * ks + c * 16 : kOobOffset);
     }
 #pragma unroll
     for (int i = 0; i < C::VIT; ++i) {
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
       const bool ok = C::VITEMS % C::NT == 0 || it < C::VITEMS;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vst[i][r] = buf_load16(vr, ok ? base + (uint32_t)(4 * kg + r) * kRow + dc * 16 : kOobOffset);
+        vst[i][r] = buf_load16(vr, ok ? (row0 + 4 * kg + r) * vs + dc * 16 : kOobOffset);
     }
   };
 
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
   const float l_tot = wave_sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
-    T* orow = O + q_off + (size_t)q_row * D;
+    T* orow = O + b * lo.sb + h * lo.sh + (int64_t)q_row * lo.sn;
 #pragma unroll
     for (int p = 0; p < C::PVB; ++p)
 #pragma unroll

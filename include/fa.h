@@ -81,7 +81,9 @@ enum {
  *            emits the row log-sum-exp), -inf for a fully masked row.
  *   mask     NULL or a descriptor (FA_MASK_NONE is the same as NULL).
  *   scale    multiplies Q.K; must be finite and > 0 (1/sqrt(D) is usual).
- * Supported: dtype F32, F16, BF16; D in {32, 40, 128}; any N >= 1.
+ * Supported: dtype F32, F16, BF16; D in {32, 40, 128}; N >= 1 with
+ * (N + 256) * D * sizeof(dtype) < 2^32 (one head's rows are addressed with
+ * 32-bit offsets; FA_ERR_SHAPE beyond that).
  */
 FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const fa_mask_t* mask, int B, int H, int N, int D, float scale,
@@ -99,6 +101,32 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
 FA_API int fa_fwd_cross(const void* q, const void* k, const void* v, void* o, float* lse,
                         const fa_mask_t* mask, int B, int H, int Nq, int Nk, int D, float scale,
                         fa_dtype_t dtype, void* hip_stream);
+
+/*
+ * Attention forward (self- or cross-attention) on strided tensor views, so a
+ * projection output laid out [B, N, H, D] needs no transposing copy (the
+ * essay page, sections 2.1 and 5.3, and the case-study page, section 3.3,
+ * transpose it to [B, H, N, D] before the kernel).  Element (b, h, n, d) of
+ * each tensor is at base[b*stride_b + h*stride_h + n*stride_n + d]: D is
+ * contiguous, strides are in elements.
+ *   q, o: n < Nq;  k, v: n < Nk;  lse [B,H,Nq] contiguous float32 or NULL.
+ * Requirements (else FA_ERR_NULL / FA_ERR_ARG / FA_ERR_ALIGN / FA_ERR_SHAPE,
+ * nothing launched): stride pointers non-NULL; strides >= 0, stride_n > 0
+ * (o: stride_n >= D); every stride times sizeof(dtype) a multiple of 16;
+ * (rows + 256) * stride_n * sizeof(dtype) at most 2^32 - 1 for each tensor.
+ * Distinct (b, h, n) of o must not overlap.  Everything else as
+ * fa_fwd_cross; with contiguous strides the results are bitwise those of
+ * fa_fwd_cross.
+ */
+typedef struct {
+  int64_t stride_b, stride_h, stride_n;
+} fa_stride_t;
+
+FA_API int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const fa_mask_t* mask, int B, int H, int Nq, int Nk, int D,
+                          const fa_stride_t* q_strides, const fa_stride_t* k_strides,
+                          const fa_stride_t* v_strides, const fa_stride_t* o_strides,
+                          float scale, fa_dtype_t dtype, void* hip_stream);
 
 /*
  * INT8-QK / FP8-PV variant (handbook page, section "SageAttention").  Steps:

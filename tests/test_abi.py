@@ -139,3 +139,31 @@ def test_merge_validation(lib):
     assert call(dtype=9) == fa.FA_ERR_UNSUPPORTED
     assert call(o=P + 8) == fa.FA_ERR_ALIGN
     assert call(lse=P + 2) == fa.FA_ERR_ALIGN
+
+
+def test_strided_validation(lib):
+    ok = fa.fa_stride_t(4 * 100 * 8 * 128, 128, 8 * 128)     # [B, N, H, D] view, H = 8, D = 128
+
+    def call(q=ok, k=ok, v=ok, o=ok, **kw):
+        a = dict(ptr=P, Nq=100, Nk=100, D=128, dtype=fa.FA_BF16)
+        a.update(kw)
+        ref = [None if s is None else ctypes.byref(s) for s in (q, k, v, o)]
+        return fa.fa_fwd_strided(a["ptr"], P, P, P, None, None, 4, 8, a["Nq"], a["Nk"], a["D"], *ref,
+                                 0.1, a["dtype"], None)
+    assert call(q=None) == fa.FA_ERR_NULL
+    assert call(o=None) == fa.FA_ERR_NULL
+    assert call(k=fa.fa_stride_t(-1, 128, 1024)) == fa.FA_ERR_ARG
+    assert call(v=fa.fa_stride_t(0, 0, 0)) == fa.FA_ERR_ARG
+    assert call(o=fa.fa_stride_t(0, 128, 64)) == fa.FA_ERR_ARG          # output rows overlap
+    assert call(q=fa.fa_stride_t(0, 128, 1028)) == fa.FA_ERR_ALIGN       # rows not 16-byte aligned
+    assert call(k=fa.fa_stride_t(4, 128, 1024)) == fa.FA_ERR_ALIGN       # batch base not aligned
+    assert call(Nk=1 << 21, k=fa.fa_stride_t(0, 0, 1 << 10)) == fa.FA_ERR_SHAPE   # 4 GiB range
+    assert call(Nq=0) == fa.FA_ERR_SHAPE
+    assert call(D=64) == fa.FA_ERR_UNSUPPORTED
+    assert call(dtype=5) == fa.FA_ERR_UNSUPPORTED
+    assert call(ptr=None) == fa.FA_ERR_NULL
+
+
+def test_contiguous_range_limit(lib):
+    # rows * D * 2 bytes beyond the 32-bit buffer range of one (b, h) head
+    assert _fwd(N=1 << 24, D=128) == fa.FA_ERR_SHAPE

@@ -105,7 +105,9 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 #ifndef FA_DMA_MINB
 #define FA_DMA_MINB (8 / FA_DMA_NW)
 #endif
-    constexpr int NW = FA_DMA_NW, BC = FA_DMA_BC, MINB = FA_DMA_MINB;
+    // additive masks load one mask value per score: 64-key tiles keep those
+    // loads within the register budget
+    constexpr int NW = FA_DMA_NW, BC = (MASK == fa::kMaskAdd) ? 64 : FA_DMA_BC, MINB = FA_DMA_MINB;
     using C = fa::DmaCfg<T, BC, NW>;
     const int nqt = (Nq + C::BR - 1) / C::BR;
     const int grid = B * H * nqt;

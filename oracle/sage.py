@@ -26,6 +26,13 @@ way on both sides:
     unquantised P), acc = acc * exp(m_{j-1} - m_j) + sum_t e4m3(448 P_t) v8_t.
   * O = acc * sv / (448 l); a row with every key masked gives O = 0.
 
+A second P V mode (``pv="bf16"`` or ``"f16"``) keeps the INT8 Q K^T steps and
+runs P V in 16 bits: V is used as given (the 16-bit input values, not
+quantised), P is rounded to the 16-bit type (round to nearest even) against
+the same running max, acc = acc * exp(m_{j-1} - m_j) + sum_t round16(P_t) V_t,
+O = acc / l (l again from the unrounded P).  This is the INT8-QK / FP16-PV
+form of the method; the readings above apply unchanged.
+
 The score, exp and accumulation steps run in float64; the quantisers use the
 float32 steps written above, reproduced with numpy float32 (IEEE, correctly
 rounded per operation).
@@ -34,7 +41,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .rounding import round_e4m3
+from .rounding import round_bf16, round_e4m3, round_f16
 
 QBLOCK = 64          # tokens per INT8 scale block
 E4M3_MAX = 448.0
@@ -83,13 +90,22 @@ def quantise_head(q_head, k_head, v_head):
     q8, sq = quantise_int8_blocks(q_head)
     k8, sk = quantise_int8_blocks(ks)
     v8, sv = quantise_fp8_channels(v_head)
-    return dict(kmean=km, ks=ks, q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv)
+    return dict(kmean=km, ks=ks, q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv,
+                v16=np.asarray(v_head, dtype=np.float64))
 
 
 def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quantise_p=True,
-                              return_lse=False):
+                              return_lse=False, pv="fp8"):
     """Blocked recurrence over key tiles with P quantised against the running max.
-    The lse is that of the quantised, smoothed scores (natural log)."""
+    The lse is that of the quantised, smoothed scores (natural log).  pv selects
+    the P V arithmetic: "fp8" (448 P and V in e4m3) or "bf16" / "f16" (P rounded
+    to that type, V unquantised)."""
+    if pv == "fp8":
+        vmat, pmul, pround = qz["v8"], E4M3_MAX, round_e4m3
+    elif pv in ("bf16", "f16"):
+        vmat, pmul, pround = qz["v16"], 1.0, (round_bf16 if pv == "bf16" else round_f16)
+    else:
+        raise ValueError(f"unknown P V mode {pv!r}")
     row_ids = np.asarray(row_ids, dtype=np.int64)
     q8 = qz["q8"][row_ids].astype(np.float64)
     k8 = qz["k8"].astype(np.float64)
@@ -101,7 +117,7 @@ def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quanti
     if key_len is not None:
         s[:, int(key_len):] = -np.inf
     R = len(row_ids)
-    D = qz["v8"].shape[1]
+    D = vmat.shape[1]
     m = np.full((R, 1), -np.inf)
     l = np.zeros((R, 1))
     acc = np.zeros((R, D))
@@ -112,27 +128,30 @@ def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quanti
         p = np.exp(st - ref)
         alpha = np.exp(m - ref)
         l = l * alpha + p.sum(axis=1, keepdims=True)
-        p8 = round_e4m3(p * E4M3_MAX) if quantise_p else p * E4M3_MAX
-        acc = acc * alpha + p8 @ qz["v8"][j:j + kv_block]
+        pq = pround(p * pmul) if quantise_p else p * pmul
+        acc = acc * alpha + pq @ vmat[j:j + kv_block]
         m = m_new
     with np.errstate(invalid="ignore", divide="ignore"):
-        o = acc * qz["sv"].astype(np.float64)[None, :] / (E4M3_MAX * l)
+        if pv == "fp8":
+            o = acc * qz["sv"].astype(np.float64)[None, :] / (E4M3_MAX * l)
+        else:
+            o = acc / l
         lse = np.where(l[:, 0] == 0, -np.inf, m[:, 0] + np.log(l[:, 0]))
     o = np.where(l == 0, 0.0, o)
     return (o, lse) if return_lse else o
 
 
 def emulate_rows(q_head, k_head, v_head, row_ids, scale, kv_block, key_len=None, qz=None,
-                 return_lse=False):
+                 return_lse=False, pv="fp8"):
     """Quantised-variant output for selected query rows of one head (float64, before
     the output rounding); with return_lse also the rows' log-sum-exp of the
     smoothed quantised scores."""
     if qz is None:
         qz = quantise_head(q_head, k_head, v_head)
-    return _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len, return_lse=return_lse)
+    return _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len, return_lse=return_lse, pv=pv)
 
 
-def emulate(q, k, v, scale, kv_block, key_len=None, return_lse=False):
+def emulate(q, k, v, scale, kv_block, key_len=None, return_lse=False, pv="fp8"):
     """Full [B, H, N, D] emulation (small shapes)."""
     q = np.asarray(q)
     B, H, N, D = q.shape
@@ -142,5 +161,5 @@ def emulate(q, k, v, scale, kv_block, key_len=None, return_lse=False):
         for h in range(H):
             kl = None if key_len is None else int(np.asarray(key_len)[b])
             out[b, h], lse[b, h] = emulate_rows(q[b, h], k[b, h], v[b, h], np.arange(N), scale, kv_block,
-                                                kl, return_lse=True)
+                                                kl, return_lse=True, pv=pv)
     return (out, lse) if return_lse else out

@@ -93,8 +93,9 @@ def _lossless_head(seed, d=8, n=256, step_q=2.0 ** -6, step_k=2.0 ** -5):
     return qc * step_q, kc * step_k, v, step_q, step_k
 
 
+@pytest.mark.parametrize("pv", ["fp8", "bf16", "f16"])
 @pytest.mark.parametrize("kv_block", [64, 128])
-def test_lossless_case_equals_unquantised_formula(kv_block):
+def test_lossless_case_equals_unquantised_formula(kv_block, pv):
     q, k, v, step_q, step_k = _lossless_head(5)
     n = len(q)
     qz = sage.quantise_head(q, k, v)
@@ -104,9 +105,50 @@ def test_lossless_case_equals_unquantised_formula(kv_block):
     # every score is an integer multiple of ln 2 within 6 ln 2 of zero, so each
     # P relative to any running max is 2^-j with j <= 12: 448 P is an e4m3 value
     scale = math.log(2) / (step_q * step_k)
-    o_emu = sage.emulate_rows(q, k, v, np.arange(n), scale, kv_block=kv_block)
+    # (P = 2^-j and V in {0, +-av/4, +-av/2, +-av} are exact in bf16 and fp16 too)
+    o_emu = sage.emulate_rows(q, k, v, np.arange(n), scale, kv_block=kv_block, pv=pv)
     o_ref, _ = attention.naive(q[None, None], k[None, None], v[None, None], scale)
     assert np.abs(o_emu - o_ref[0, 0]).max() <= 1e-12 * np.abs(v).max()
+
+
+def test_identity_quantisers_reduce_to_blocked_oracle_16bit_pv():
+    rng = np.random.default_rng(16)
+    n, d = 130, 16
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    qz = dict(q8=q, sq=np.ones(3), k8=k - k.mean(axis=0), sk=np.ones(3), v16=v)
+    for pv in ("bf16", "f16"):
+        o_id = sage._quantised_attention_rows(np.arange(n), qz, 0.25, 64, quantise_p=False, pv=pv)
+        o_bl, _ = attention.blocked(q[None, None], k[None, None], v[None, None], 0.25, block=64)
+        assert np.abs(o_id - o_bl[0, 0]).max() < 1e-12
+
+
+@pytest.mark.parametrize("pv,ulp", [("bf16", 2.0 ** -8), ("f16", 2.0 ** -11)])
+def test_16bit_pv_constant_v_bound(pv, ulp):
+    """With V constant per channel, O = c * (sum of rounded P) / (sum of P):
+    within one half-ulp of the P type of c (P rounded to nearest), and not
+    exactly c once P needs rounding."""
+    rng = np.random.default_rng(21)
+    n, d = 300, 8
+    q, k = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(2))
+    c = rng.standard_normal(d)
+    v = np.broadcast_to(c, (n, d)).copy()
+    o = sage.emulate_rows(q, k, v, np.arange(n), 0.5, 64, pv=pv)
+    rel = np.abs(o / c[None, :] - 1.0)
+    assert rel.max() <= ulp / 2 * 1.0000001
+    assert rel.max() > ulp / 100            # P really was rounded (fp64 noise is ~1e-16)
+
+
+def test_16bit_pv_is_closer_than_fp8_on_wan_recipe():
+    from attention_fa_fwd_04_amd.workloads import WORKLOADS, head
+    w = WORKLOADS[5].with_shape(N=1200)
+    q, k, v = (head(w, t, 0, 0).double().numpy() for t in range(3))
+    rows = np.arange(0, 1200, 7)
+    ref = attention.rows(q[rows], k, v, w.scale)[0]
+    def cos(o):
+        return float((o * ref).sum() / np.sqrt((o * o).sum() * (ref * ref).sum()))
+    c8 = cos(sage.emulate_rows(q, k, v, rows, w.scale, 64, pv="fp8"))
+    c16 = cos(sage.emulate_rows(q, k, v, rows, w.scale, 64, pv="bf16"))
+    assert c16 >= 0.999 and c16 >= c8
 
 
 def test_identity_quantisers_reduce_to_blocked_oracle():

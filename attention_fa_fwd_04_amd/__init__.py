@@ -24,6 +24,7 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
 FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
 
 EXPORTED = ("fa_fwd", "fa_fwd_cross", "fa_fwd_strided", "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk",
+            "fa_fwd_int8qk_pv16_workspace_bytes", "fa_fwd_int8qk_pv16",
             "fa_merge", "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
 
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
     h.fa_fwd_int8qk_workspace_bytes.restype = sz
     h.fa_fwd_int8qk.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     h.fa_fwd_int8qk.restype = i32
+    h.fa_fwd_int8qk_pv16_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    h.fa_fwd_int8qk_pv16_workspace_bytes.restype = sz
+    h.fa_fwd_int8qk_pv16.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    h.fa_fwd_int8qk_pv16.restype = i32
     h.fa_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     h.fa_merge.restype = i32
     h.fa_int8qk_kv_block.argtypes = []
@@ -115,6 +120,16 @@ def fa_fwd_int8qk(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace,
                   workspace_bytes, hip_stream) -> int:
     return lib().fa_fwd_int8qk(q, k, v, o, lse, mask, B, H, N, D, scale, dtype,
                                workspace, workspace_bytes, hip_stream)
+
+
+def fa_fwd_int8qk_pv16_workspace_bytes(B, H, N, D) -> int:
+    return lib().fa_fwd_int8qk_pv16_workspace_bytes(B, H, N, D)
+
+
+def fa_fwd_int8qk_pv16(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace,
+                       workspace_bytes, hip_stream) -> int:
+    return lib().fa_fwd_int8qk_pv16(q, k, v, o, lse, mask, B, H, N, D, scale, dtype,
+                                    workspace, workspace_bytes, hip_stream)
 
 
 def fa_merge(o_a, lse_a, o_b, lse_b, o, lse, B, H, N, D, dtype, hip_stream) -> int:
@@ -240,25 +255,31 @@ def fwd(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
 
 
 def fwd_int8qk(q, k, v, *, key_len=None, scale: Optional[float] = None,
-               return_lse: bool = False, workspace=None, out=None):
-    """The INT8-QK / FP8-PV variant for GPU tensors [B, H, N, 128] (bf16 / fp16)."""
+               return_lse: bool = False, workspace=None, out=None, pv: str = "fp8"):
+    """The INT8-QK variant for GPU tensors [B, H, N, 128] (bf16 / fp16): P V
+    in FP8 (pv="fp8", fa_fwd_int8qk) or in the input's 16-bit type
+    (pv="16", fa_fwd_int8qk_pv16)."""
     import torch
+    if pv not in ("fp8", "16"):
+        raise ValueError('pv must be "fp8" or "16"')
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
-    need = fa_fwd_int8qk_workspace_bytes(B, H, N, D)
+    size_fn, entry, where = ((fa_fwd_int8qk_workspace_bytes, fa_fwd_int8qk, "fa_fwd_int8qk") if pv == "fp8" else
+                             (fa_fwd_int8qk_pv16_workspace_bytes, fa_fwd_int8qk_pv16, "fa_fwd_int8qk_pv16"))
+    need = size_fn(B, H, N, D)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
     keep = []
     m = _mask_struct(q, None, key_len, keep)
     st = torch.cuda.current_stream(q.device).cuda_stream
-    rc = fa_fwd_int8qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                       lse.data_ptr() if lse is not None else None,
-                       ctypes.byref(m) if m is not None else None,
-                       B, H, N, D, scale, _dtype_code(q), ws.data_ptr(), ws.numel(), st)
+    rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+               lse.data_ptr() if lse is not None else None,
+               ctypes.byref(m) if m is not None else None,
+               B, H, N, D, scale, _dtype_code(q), ws.data_ptr(), ws.numel(), st)
     if rc != FA_OK:
-        raise FAError(rc, "fa_fwd_int8qk")
+        raise FAError(rc, where)
     return (o, lse) if return_lse else o
 
 

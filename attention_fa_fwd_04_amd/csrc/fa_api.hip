@@ -250,31 +250,66 @@ FA_API size_t fa_fwd_int8qk_workspace_bytes(int B, int H, int N, int D) {
   return fa::int8qk_workspace_layout(B, H, N, D).total;
 }
 
-FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, float* lse,
-                  const fa_mask_t* mask, int B, int H, int N, int D, float scale,
-                  fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                  void* hip_stream) {
+FA_API size_t fa_fwd_int8qk_pv16_workspace_bytes(int B, int H, int N, int D) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return 0;
+  return fa::int8qk_workspace_layout(B, H, N, D, true).total;
+}
+
+}  // extern "C"
+
+namespace {
+int int8qk_common(bool pv16, const void* q, const void* k, const void* v, void* o, float* lse,
+                  const fa_mask_t* mask, int B, int H, int N, int D, float scale, fa_dtype_t dtype,
+                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const char* name = pv16 ? "fa_fwd_int8qk_pv16" : "fa_fwd_int8qk";
   int rc = check_common(q, k, v, o, lse, mask, B, H, N, D, scale);
   if (rc != FA_OK) return rc;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (D != 128) return FA_ERR_UNSUPPORTED;
   const int kind = mask ? mask->kind : FA_MASK_NONE;
   if (kind == FA_MASK_ADDITIVE) return FA_ERR_UNSUPPORTED;
-  const fa::Int8Layout lay = fa::int8qk_workspace_layout(B, H, N, D);
+  if ((int64_t)(N + 256) * D * 2 > (int64_t)UINT32_MAX) return FA_ERR_SHAPE;
+  const fa::Int8Layout lay = fa::int8qk_workspace_layout(B, H, N, D, pv16);
   if (!workspace) return FA_ERR_WORKSPACE;
   if (workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
   const int* key_len = (kind == FA_MASK_KEYLEN) ? static_cast<const int*>(mask->ptr) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (log_enabled())
-    std::fprintf(stderr, "[fa] fa_fwd_int8qk dtype=%s D=%d keylen=%d B=%d H=%d N=%d ws=%zu\n",
-                 dtype_name(dtype), D, key_len != nullptr, B, H, N, lay.total);
-  if (dtype == FA_BF16)
-    rc = fa::launch_int8qk<__bf16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
-  else
-    rc = fa::launch_int8qk<_Float16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+    std::fprintf(stderr, "[fa] %s dtype=%s D=%d keylen=%d B=%d H=%d N=%d ws=%zu\n",
+                 name, dtype_name(dtype), D, key_len != nullptr, B, H, N, lay.total);
+  if (pv16) {
+    if (dtype == FA_BF16)
+      rc = fa::launch_int8qk_pv16<__bf16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+    else
+      rc = fa::launch_int8qk_pv16<_Float16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+  } else {
+    if (dtype == FA_BF16)
+      rc = fa::launch_int8qk<__bf16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+    else
+      rc = fa::launch_int8qk<_Float16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+  }
   if (rc != FA_OK) return rc;
-  return record_launch("fa_fwd_int8qk");
+  return record_launch(name);
+}
+}  // namespace
+
+extern "C" {
+
+FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                  fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                  void* hip_stream) {
+  return int8qk_common(false, q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace, workspace_bytes,
+                       hip_stream);
+}
+
+FA_API int fa_fwd_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                              fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              void* hip_stream) {
+  return int8qk_common(true, q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace, workspace_bytes,
+                       hip_stream);
 }
 
 FA_API int fa_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,

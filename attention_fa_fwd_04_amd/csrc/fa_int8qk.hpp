@@ -41,7 +41,8 @@ struct Int8Layout {
   size_t total;
 };
 
-inline Int8Layout int8qk_workspace_layout(int B, int H, int N, int D) {
+// pv16: the INT8-QK / 16-bit-PV form keeps V^T in the input's 16-bit type.
+inline Int8Layout int8qk_workspace_layout(int B, int H, int N, int D, bool pv16 = false) {
   Int8Layout L{};
   const size_t bh = (size_t)B * H;
   L.npad = (N + kQBlock - 1) / kQBlock * kQBlock;
@@ -53,7 +54,7 @@ inline Int8Layout int8qk_workspace_layout(int B, int H, int N, int D) {
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return at; };
   L.q8 = take(bh * L.npad * D);                    // int8 [BH, npad, D]
   L.k8 = take(bh * L.npad * D);                    // int8 [BH, npad, D]
-  L.v8t = take(bh * (size_t)D * L.npad);           // e4m3 [BH, D, npad]
+  L.v8t = take(bh * (size_t)D * L.npad * (pv16 ? 2 : 1));   // e4m3 (or 16-bit) [BH, D, npad]
   L.sq = take(bh * L.groups * 4);                  // f32 [BH, groups]
   L.sk = take(bh * L.groups * 4);
   L.sv = take(bh * (size_t)D * 4);                 // f32 [BH, D]  av / 448
@@ -224,6 +225,45 @@ __global__ __launch_bounds__(256) void int8_quant_v_kernel(
   uint8_t* dst = v8t + ((size_t)bh * D + d) * npad + (size_t)g * kQBlock + 32 * half;
   *reinterpret_cast<u32x4*>(dst) = lo;
   *reinterpret_cast<u32x4*>(dst + 16) = hi;
+}
+
+// Position of key k (0..31) inside its 32-key block of the 16-bit V^T: the
+// 32x32x16 P V MFMA takes, from lane half h and step cc, the 8 scores the
+// lane holds for keys 16 cc + 4 h + {0..3} and 16 cc + 8 + 4 h + {0..3}; with
+// key 8g + 4h + r stored at 16h + 4g + r those are 8 consecutive positions.
+__host__ __device__ constexpr int v16_pos(int k) {
+  return 16 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3);
+}
+
+// One 64-token block of V (16-bit, unquantised), transposed into
+// V^T[d][64 g + 32 (k >> 5) + v16_pos(k & 31)]; keys >= N are zero.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void int8_v16t_kernel(
+    const T* __restrict__ V, T* __restrict__ vt, int N, int npad) {
+  static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
+  constexpr int TS = 64 + 8;                    // LDS row: 64 keys + pad (elements)
+  __shared__ __attribute__((aligned(16))) T tile[D * TS];
+  const int g = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const T* Vh = V + (size_t)bh * N * D;
+  // thread: key k = t / 4, channels 32 * (t % 4) .. +31
+  const int k = t >> 2, c0 = 32 * (t & 3);
+  const int row = g * kQBlock + k;
+  const int pos = 32 * (k >> 5) + v16_pos(k & 31);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (row < N) raw = *reinterpret_cast<const u32x4*>(Vh + (size_t)row * D + c0 + 8 * q);
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[(c0 + 8 * q + e) * TS + pos] = v[e];
+  }
+  __syncthreads();
+  // thread: channel d = t / 2, 32 positions (t % 2)
+  const int d = t >> 1, half = t & 1;
+  T* dst = vt + ((size_t)bh * D + d) * npad + (size_t)g * kQBlock + 32 * half;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    *reinterpret_cast<u32x4*>(dst + 8 * c) = *reinterpret_cast<const u32x4*>(tile + d * TS + 32 * half + 8 * c);
 }
 
 // ---------------------------------------------------------------- main kernel
@@ -423,6 +463,236 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
       LSE[(size_t)bh * N + q_row] =
           l_tot > 0.f ? (m_run + log2f(l_tot) - kLog2_448) * kLn2 : -INFINITY;
   }
+}
+
+// INT8-QK / 16-bit-PV form: the same Q K^T and online softmax as
+// fa_int8qk_kernel, with P rounded to the input's 16-bit type (P <= 1 against
+// the running max) and V^T read unquantised from the workspace (keys permuted
+// per 32 by v16_pos); P V runs on the 16-bit 32x32x16 MFMA, four per 32
+// channels per 64-key tile.
+template <typename T, int MASKLEN>
+__global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
+    const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const T* __restrict__ vt,
+    const float* __restrict__ sq, const float* __restrict__ sk,
+    const int* __restrict__ key_len, T* __restrict__ O, float* __restrict__ LSE,
+    int H, int N, int npad, int groups, int nqt, float c_log2) {
+  constexpr int D = 128, BC = kInt8Bc, BR = 128, NT = 256;
+  constexpr int KSTR = D + 16;                  // int8 K row + pad
+  constexpr int VSTR = 2 * BC + 16;             // 16-bit V^T row (64 keys) + pad
+  constexpr int KBYTES = BC * KSTR, VBYTES = D * VSTR, BUF = KBYTES + VBYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 31, lh = lane >> 5;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / nqt, qt = logical - bh * nqt;
+  const int b = bh / H;
+
+  int n_eff = N;
+  if constexpr (MASKLEN) {
+    const int L = key_len[b];
+    n_eff = L < 0 ? 0 : (L > N ? N : L);
+  }
+  const int ntiles = (n_eff + BC - 1) / BC;
+
+  const int8_t* Qh = q8 + (size_t)bh * npad * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k8 + (size_t)bh * npad * D, (uint32_t)npad * D);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vt + (size_t)bh * D * npad, (uint32_t)D * npad * 2);
+
+  const int q_row = qt * BR + wave * 32 + ln;
+  const bool q_ok = q_row < N;
+  // rows past N are zero codes in the workspace (npad >= q_row + 1 within the tile)
+  u32x4 qreg[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    qreg[s] = *reinterpret_cast<const u32x4*>(Qh + (size_t)min(q_row, npad - 1) * D + (2 * s + lh) * 16);
+  // every query of a wave lies in one 64-token scale block
+  const float sq_w = sq[(size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)];
+  const float* skh = sk + (size_t)bh * groups;
+
+  // staging: K tile 64 rows x 8 chunks (2 per thread), V^T tile 128 rows x 8
+  // chunks (4 per thread)
+  u32x4 kst[2], vst[4];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) kst[i] = buf_load16(kr, (uint32_t)(j * BC) * D + (tid + NT * i) * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int it = tid + NT * i;
+      const int d = it >> 3, c = it & 7;
+      vst[i] = buf_load16(vr, ((uint32_t)d * npad + j * BC) * 2 + c * 16);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint8_t* kb = smem + buf * BUF;
+    uint8_t* vb = kb + KBYTES;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int it = tid + NT * i;
+      *reinterpret_cast<u32x4*>(kb + (it >> 3) * KSTR + (it & 7) * 16) = kst[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int it = tid + NT * i;
+      *reinterpret_cast<u32x4*>(vb + (it >> 3) * VSTR + (it & 7) * 16) = vst[i];
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[p][i] = 0.f;
+
+  auto step = [&](int j, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int buf = j & 1;
+    load_tile(j + 1);
+    const uint8_t* kb = smem + buf * BUF;
+    const uint8_t* vb = kb + KBYTES;
+    const int kv0 = j * BC;
+    const float c = sq_w * skh[j] * c_log2;       // one K scale block per tile
+
+    i32x16 si[2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) si[G][i] = 0;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * G + ln) * KSTR + (2 * st + lh) * 16);
+        si[G] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                      __builtin_bit_cast(i32x4, qreg[st]), si[G], 0, 0, 0);
+      }
+    }
+    // Full tiles: the row max is taken on the exact int32 sums and scaled once
+    // (the tile's scale c is >= 0), and the scale is folded into the exp2 FMA.
+    // The ragged last tile scales first so dropped keys can be -inf.
+    float s[32];
+    float mx;
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
+          s[16 * G + i] = key < n_eff ? (float)si[G][i] * c : -INFINITY;
+        }
+      mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) mx = fmaxf(mx, s[i]);
+    } else {
+      int imx = si[0][0];
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          imx = max(imx, si[G][i]);
+          s[16 * G + i] = (float)si[G][i];
+        }
+      mx = (float)imx * c;
+    }
+    mx = wave_max_halves(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+      l_run *= alpha;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[p][i] *= alpha;
+    }
+    // P = exp2(s - m) <= 1, rounded to the 16-bit type for the P V operand
+    auto pexp = [&](float x) {
+      return MASKED ? __builtin_amdgcn_exp2f(x - m_use) : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -m_use));
+    };
+    float psum = 0.f;
+    float pv[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      pv[i] = pexp(s[i]);
+      psum += pv[i];
+    }
+    l_run += psum;
+    // P^T operand for (key block G, 8-key half cc): the lane's scores
+    // 16 G + 8 cc .. +7, keys 32 G + 16 cc + {0..3, 8..11} + 4 lh; the V^T
+    // operand holds the same keys at positions 16 lh + 8 cc .. +7 of block G.
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const u32x4 bop = pack_chunk<T>(pv + 16 * G + 8 * cc);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const u32x4 aop = *reinterpret_cast<const u32x4*>(vb + (32 * p + ln) * VSTR + (32 * G + 16 * lh + 8 * cc) * 2);
+          acc[p] = mfma_chunk<T>(aop, bop, acc[p]);
+        }
+      }
+    store_tile(buf ^ 1);
+    __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  const int nfull = n_eff / BC;
+  for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});
+  if (nfull < ntiles) step(nfull, BoolTag<true>{});
+
+  const float l_tot = wave_sum_halves(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (q_ok) {
+    T* orow = O + ((size_t)bh * N + q_row) * D;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * p + 8 * g + 4 * lh;
+        store4<T>(orow + d0, acc[p][4 * g] * inv, acc[p][4 * g + 1] * inv,
+                  acc[p][4 * g + 2] * inv, acc[p][4 * g + 3] * inv);
+      }
+    if (LSE != nullptr && lh == 0)
+      LSE[(size_t)bh * N + q_row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename T>
+int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse, const int* key_len,
+                       int B, int H, int N, float scale, void* workspace, const Int8Layout& L, hipStream_t st) {
+  constexpr int D = 128;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* q8 = reinterpret_cast<int8_t*>(ws + L.q8);
+  int8_t* k8 = reinterpret_cast<int8_t*>(ws + L.k8);
+  T* vt = reinterpret_cast<T*>(ws + L.v8t);
+  float* sq = reinterpret_cast<float*>(ws + L.sq);
+  float* sk = reinterpret_cast<float*>(ws + L.sk);
+  float* sv = reinterpret_cast<float*>(ws + L.sv);
+  float* vmul = reinterpret_cast<float*>(ws + L.vmul);
+  float* kmean = reinterpret_cast<float*>(ws + L.kmean);
+  double* kpart = reinterpret_cast<double*>(ws + L.kpart);
+  float* vpart = reinterpret_cast<float*>(ws + L.vpart);
+  const T* Q = static_cast<const T*>(q);
+  const T* K = static_cast<const T*>(k);
+  const T* V = static_cast<const T*>(v);
+  const int BH = B * H;
+  hipLaunchKernelGGL((int8_stats_kernel<T, D>), dim3(L.splits, BH), dim3(256), 0, st, K, V, kpart, vpart, N, L.splits,
+                     L.split_rows);
+  hipLaunchKernelGGL((int8_finalize_kernel<D>), dim3(BH), dim3(D), 0, st, kpart, vpart, kmean, sv, vmul, N, L.splits);
+  hipLaunchKernelGGL((int8_quant_qk_kernel<T, D>), dim3(L.groups, BH, 2), dim3(256), 0, st, Q, K, kmean, q8, k8, sq, sk,
+                     N, L.npad, L.groups);
+  hipLaunchKernelGGL((int8_v16t_kernel<T, D>), dim3(L.groups, BH), dim3(256), 0, st, V, vt, N, L.npad);
+  const int nqt = (N + 127) / 128;
+  const int grid = BH * nqt;
+  if (key_len)
+    hipLaunchKernelGGL((fa_int8qk_pv16_kernel<T, 1>), dim3(grid), dim3(256), 0, st, q8, k8, vt, sq, sk, key_len,
+                       static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
+  else
+    hipLaunchKernelGGL((fa_int8qk_pv16_kernel<T, 0>), dim3(grid), dim3(256), 0, st, q8, k8, vt, sq, sk, key_len,
+                       static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
+  return FA_OK;
 }
 
 template <typename T>

@@ -49,6 +49,7 @@ class Workload:
     outlier_scale: float = 8.0
     k_offset_var: float = 0.0    # per-(b,h,channel) K offset ~ N(0, var)
     quantised: bool = False      # run through the INT8-QK / FP8-PV entry point
+    pv16: bool = False           # with quantised: the INT8-QK / 16-bit-PV form instead
     sampled_rows: int = 0        # rows the oracle checks at full size (0 = all)
     Nk: int = 0                  # key / value length when it differs from N (cross-attention)
     merge: bool = False          # time the merge of two partial results of this shape

@@ -145,8 +145,10 @@ def main() -> int:
         kl = None if inp["key_len"] is None else inp["key_len"].to(dev)
         o = torch.empty_like(q)
         if w.quantised:
-            ws = torch.empty(fa.fa_fwd_int8qk_workspace_bytes(w.B, w.H, w.N, w.D), dtype=torch.uint8, device=dev)
-            call = lambda: fa.fwd_int8qk(q, k, v, key_len=kl, workspace=ws, out=o)  # noqa: E731
+            size = fa.fa_fwd_int8qk_pv16_workspace_bytes if w.pv16 else fa.fa_fwd_int8qk_workspace_bytes
+            ws = torch.empty(size(w.B, w.H, w.N, w.D), dtype=torch.uint8, device=dev)
+            pv = "16" if w.pv16 else "fp8"
+            call = lambda: fa.fwd_int8qk(q, k, v, key_len=kl, workspace=ws, out=o, pv=pv)  # noqa: E731
         else:
             call = lambda: fa.fwd(q, k, v, key_len=kl, out=o)  # noqa: E731
         return timed(call, steps, warmup)
@@ -234,6 +236,9 @@ def main() -> int:
                 b_ms, _ = measure(wb, 3, 1)
                 extra[wx.name]["bf16_same_inputs_ms"] = round(b_ms, 3)
                 extra[wx.name]["bf16_same_inputs_tflops"] = round(fl / (b_ms * 1e-3) / 1e12, 2)
+                p_ms, _ = measure(wx.with_shape(pv16=True), 3, 1)
+                extra[wx.name]["int8qk_pv16_ms"] = round(p_ms, 3)
+                extra[wx.name]["int8qk_pv16_tops"] = round(fl / (p_ms * 1e-3) / 1e12, 2)
         out["extra"] = extra
     print(json.dumps(out), flush=True)
     return 0

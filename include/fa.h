@@ -171,6 +171,24 @@ FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, f
                   void* hip_stream);
 
 /*
+ * INT8-QK / 16-bit-PV form of the same method: steps 1, 2, 4 and 5 as for
+ * fa_fwd_int8qk, then P (<= 1 against the running max) rounded to `dtype`
+ * and multiplied with V as given (not quantised) on 16-bit matrix cores with
+ * float32 accumulation; O = acc / l, l summing the unrounded P.  More
+ * accurate than the FP8 form and slower in P V.  lse as for fa_fwd_int8qk.
+ * Same arguments and support as fa_fwd_int8qk; its workspace
+ * (fa_fwd_int8qk_pv16_workspace_bytes) has the same regions in the same
+ * order except v8t, which holds V^T in `dtype`: [BH, D, Np], row d,
+ * position 64g + 32(k >> 5) + pi16(k & 31) holds key 64g + k,
+ * pi16(k) = 16*((k>>2)&1) + 4*(k>>3) + (k&3).
+ */
+FA_API size_t fa_fwd_int8qk_pv16_workspace_bytes(int B, int H, int N, int D);
+FA_API int fa_fwd_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                              fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              void* hip_stream);
+
+/*
  * Merge two attention results computed for the same queries over disjoint
  * key sets (K/V split along the sequence, as in ring attention: essay page,
  * section 6.2):

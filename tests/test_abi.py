@@ -167,3 +167,23 @@ def test_strided_validation(lib):
 def test_contiguous_range_limit(lib):
     # rows * D * 2 bytes beyond the 32-bit buffer range of one (b, h) head
     assert _fwd(N=1 << 24, D=128) == fa.FA_ERR_SHAPE
+
+
+def test_int8qk_pv16_validation(lib):
+    ws = fa.fa_fwd_int8qk_pv16_workspace_bytes(1, 2, 1000, 128)
+    assert ws > fa.fa_fwd_int8qk_workspace_bytes(1, 2, 1000, 128)     # 16-bit V^T region
+    assert fa.fa_fwd_int8qk_pv16_workspace_bytes(1, 0, 1000, 128) == 0
+
+    def call(**kw):
+        a = dict(dtype=fa.FA_BF16, D=128, ws=P, wsb=ws, mask=None, N=1000)
+        a.update(kw)
+        return fa.fa_fwd_int8qk_pv16(P, P, P, P, None, a["mask"], 1, 2, a["N"], a["D"], 0.1, a["dtype"],
+                                     a["ws"], a["wsb"], None)
+    assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert call(D=40) == fa.FA_ERR_UNSUPPORTED
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=fa.fa_fwd_int8qk_workspace_bytes(1, 2, 1000, 128)) == fa.FA_ERR_WORKSPACE
+    assert call(ws=P + 16) == fa.FA_ERR_ALIGN
+    assert call(N=1 << 24) == fa.FA_ERR_SHAPE
+    add = fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P, 0, 0, 0, 1)
+    assert call(mask=ctypes.byref(add)) == fa.FA_ERR_UNSUPPORTED

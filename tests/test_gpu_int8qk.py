@@ -1,5 +1,6 @@
-"""Parity of the INT8-QK / FP8-PV entry point (fa_fwd_int8qk) with the oracle's
-exact emulation, and of its quantised operands with the oracle's quantisers.
+"""Parity of the INT8-QK entry points (fa_fwd_int8qk: FP8 P V;
+fa_fwd_int8qk_pv16: 16-bit P V) with the oracle's exact emulation, and of
+their quantised operands with the oracle's quantisers.
 
 The quantised codes and scales are decided in float32 by the same steps on
 both sides (the K mean is summed in float64 on both sides and rounded once),
@@ -38,12 +39,12 @@ def _a256(x):
     return (x + 255) // 256 * 256
 
 
-def layout(B, H, N, D):
+def layout(B, H, N, D, vbytes=1):
     """Region offsets of the workspace as documented in include/fa.h."""
     bh, npad = B * H, (N + 63) // 64 * 64
     g = npad // 64
     off, out = 0, {}
-    for name, nbytes in (("q8", bh * npad * D), ("k8", bh * npad * D), ("v8t", bh * D * npad),
+    for name, nbytes in (("q8", bh * npad * D), ("k8", bh * npad * D), ("v8t", bh * D * npad * vbytes),
                          ("sq", bh * g * 4), ("sk", bh * g * 4), ("sv", bh * D * 4),
                          ("vmul", bh * D * 4), ("kmean", bh * D * 4)):
         out[name] = (off, nbytes)
@@ -55,10 +56,14 @@ def v8_pos(k):
     return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3)
 
 
-def run(dev, inp, key_len=None, ws=None):
+def v16_pos(k):
+    return 32 * (k >> 5) + 16 * ((k >> 2) & 1) + 4 * ((k >> 3) & 3) + (k & 3)
+
+
+def run(dev, inp, key_len=None, ws=None, pv="fp8"):
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     kl = None if key_len is None else key_len.to(dev)
-    o, lse = fa.fwd_int8qk(q, k, v, key_len=kl, return_lse=True, workspace=ws)
+    o, lse = fa.fwd_int8qk(q, k, v, key_len=kl, return_lse=True, workspace=ws, pv=pv)
     torch.cuda.synchronize()
     return o, lse
 
@@ -150,6 +155,103 @@ def test_int8qk_wan_full(dev):
         ids = rows[rows[:, 1] == h][:, 2]
         qh, kh, vh = (inp[n][0, h].double().numpy() for n in ("q", "k", "v"))
         ref = sage.emulate_rows(qh, kh, vh, ids, w.scale, fa.fa_int8qk_kv_block())
+        un, _ = attention.rows(qh[ids], kh, vh, w.scale)
+        got = o_c[0, h, ids].double().numpy()
+        errs.append(np.abs(got - ref))
+        got_all.append(got)
+        un_all.append(un)
+    err = np.concatenate([e.ravel() for e in errs])
+    g = np.concatenate(got_all).ravel()
+    u = np.concatenate(un_all).ravel()
+    cos = g @ u / np.linalg.norm(g) / np.linalg.norm(u)
+    say(f"  {len(rows)} rows max|err|={err.max():.3e} mean|err|={err.mean():.3e} cosine={cos:.5f}")
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3
+    assert cos >= 0.99
+
+
+# ---- INT8-QK / 16-bit-PV (fa_fwd_int8qk_pv16) ----
+
+EMU_PV = {"bf16": "bf16", "f16": "f16"}
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_pv16_operands_bit_exact(dev, dt):
+    w = WORKLOADS[5].with_shape(H=2, N=1000, dtype=dt)
+    inp = make_inputs(w)
+    B, H, N, D = w.B, w.H, w.N, w.D
+    ws = torch.empty(fa.fa_fwd_int8qk_pv16_workspace_bytes(B, H, N, D), dtype=torch.uint8, device=dev)
+    run(dev, inp, ws=ws, pv="16")
+    buf = ws.cpu().numpy()
+    lay, npad = layout(B, H, N, D, vbytes=2)
+
+    def region(name, dtype, shape):
+        off, nbytes = lay[name]
+        return buf[off:off + nbytes].view(dtype).reshape(shape)
+
+    q8 = region("q8", np.int8, (B * H, npad, D))
+    k8 = region("k8", np.int8, (B * H, npad, D))
+    vt = region("v8t", np.uint16, (B * H, D, npad))
+    sq = region("sq", np.float32, (B * H, npad // 64))
+    sk = region("sk", np.float32, (B * H, npad // 64))
+    perm = np.array([v16_pos(k) for k in range(64)])
+    vbits = inp["v"].view(torch.int16).numpy().astype(np.uint16)
+    for h in range(H):
+        qz = sage.quantise_head(inp["q"][0, h].double().numpy(), inp["k"][0, h].double().numpy(),
+                                inp["v"][0, h].double().numpy())
+        assert np.array_equal(q8[h, :N], qz["q8"]) and np.array_equal(k8[h, :N], qz["k8"]), "q8/k8"
+        assert np.array_equal(sq[h], qz["sq"]) and np.array_equal(sk[h], qz["sk"]), "scales"
+        got = vt[h].reshape(D, npad // 64, 64)[:, :, perm].reshape(D, npad)     # undo the key order
+        assert np.array_equal(got[:, :N].T, vbits[0, h]), "V^T"
+        assert not got[:, N:].any(), "padding keys"
+
+
+@pytest.mark.parametrize("keylen", [False, True])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_pv16_parity_small(dev, dt, keylen):
+    for N in (1, 63, 64, 65, 200, 1000):
+        w = Workload(97, f"int8pv16-{dt}", dt, 2, 2, N, 128, k_offset_var=2.0)
+        inp = make_inputs(w)
+        kl = torch.tensor([max(1, N // 3), N], dtype=torch.int32) if keylen else None
+        say(f"case pv16 dt={dt} N={N} keylen={keylen}")
+        o, lse = run(dev, inp, key_len=kl, pv="16")
+        qn, kn, vn = (inp[n].double().numpy() for n in ("q", "k", "v"))
+        ref, ref_lse = sage.emulate(qn, kn, vn, w.scale, fa.fa_int8qk_kv_block(),
+                                    key_len=None if kl is None else kl.numpy(), return_lse=True, pv=EMU_PV[dt])
+        got = o.cpu().double().numpy()
+        err = np.abs(got - ref)
+        say(f"  max|err|={err.max():.3e} mean|err|={err.mean():.3e}")
+        assert np.all(err <= 1e-2 + HALF_ULP[w.torch_dtype] * np.abs(ref))
+        assert err.mean() <= 1e-3
+        un, _ = attention.naive(qn, kn, vn, w.scale, key_len=None if kl is None else kl.numpy())
+        cos = (got * un).sum() / np.linalg.norm(got) / np.linalg.norm(un)
+        say(f"  cosine vs unquantised {cos:.5f}")
+        assert cos >= 0.99
+        lg = lse.cpu().double().numpy()
+        assert np.array_equal(np.isneginf(lg), np.isneginf(ref_lse))
+        fin = np.isfinite(ref_lse)
+        assert np.abs(lg[fin] - ref_lse[fin]).max() < 1e-4
+
+
+def test_pv16_fully_masked_batch(dev):
+    w = Workload(98, "int8pv16-mask", "f16", 2, 2, 100, 128)
+    inp = make_inputs(w)
+    o, lse = run(dev, inp, key_len=torch.tensor([0, 100], dtype=torch.int32), pv="16")
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.isfinite(o[1]).all()
+
+
+def test_pv16_wan_full(dev):
+    w = WORKLOADS[5]
+    say(f"case pv16 {w}")
+    inp = make_inputs(w)
+    o, _ = run(dev, inp, pv="16")
+    rows = sample_rows(w, w.sampled_rows)
+    o_c = o.cpu()
+    errs, got_all, un_all = [], [], []
+    for h in sorted({int(r[1]) for r in rows}):
+        ids = rows[rows[:, 1] == h][:, 2]
+        qh, kh, vh = (inp[n][0, h].double().numpy() for n in ("q", "k", "v"))
+        ref = sage.emulate_rows(qh, kh, vh, ids, w.scale, fa.fa_int8qk_kv_block(), pv="bf16")
         un, _ = attention.rows(qh[ids], kh, vh, w.scale)
         got = o_c[0, h, ids].double().numpy()
         errs.append(np.abs(got - ref))

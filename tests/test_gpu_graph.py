@@ -1,4 +1,4 @@
-"""Both entry points can be captured in a HIP graph and replayed.
+"""Every entry point can be captured in a HIP graph and replayed.
 
 The library allocates nothing, issues no memset and never synchronises, so
 a captured call must replay to the same bits as an eager call on the same
@@ -68,3 +68,31 @@ def test_graph_replay_fa_fwd_int8qk(dev):
     o = torch.empty_like(q)
     ws = torch.empty(fa.fa_fwd_int8qk_workspace_bytes(w.B, w.H, w.N, w.D), dtype=torch.uint8, device=dev)
     _replay_matches(dev, lambda: fa.fwd_int8qk(q, k, v, workspace=ws, out=o), o)
+
+
+def test_graph_replay_cross_and_strided(dev):
+    w = WORKLOADS[6].with_shape(B=1, H=4, N=1000)                  # Nq = 1000, Nk = 77, D = 40
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    _replay_matches(dev, lambda: fa.fwd(q, k, v, out=o), o)
+    qs, ks, vs = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))   # [B, N, H, D] views
+    os_ = torch.empty_like(qs)
+    _replay_matches(dev, lambda: fa.fwd(qs, ks, vs, out=os_), os_)
+
+
+def test_graph_replay_merge(dev):
+    g = torch.Generator().manual_seed(3)
+    oa, ob = (torch.randn(1, 3, 777, 128, generator=g).to(torch.bfloat16).to(dev) for _ in range(2))
+    la, lb = (torch.randn(1, 3, 777, generator=g).to(dev) for _ in range(2))
+    o, lse = torch.empty_like(oa), torch.empty_like(la)
+    _replay_matches(dev, lambda: fa.merge(oa, la, ob, lb, out=o, out_lse=lse)[0], o)
+
+
+def test_graph_replay_int8qk_pv16(dev):
+    w = WORKLOADS[5].with_shape(H=2, N=1500)
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    ws = torch.empty(fa.fa_fwd_int8qk_pv16_workspace_bytes(w.B, w.H, w.N, w.D), dtype=torch.uint8, device=dev)
+    _replay_matches(dev, lambda: fa.fwd_int8qk(q, k, v, workspace=ws, out=o, pv="16"), o)

@@ -83,6 +83,9 @@ WORKLOADS = {
     6: Workload(6, "sd15-text-cross", "f16", 2, 8, 4096, 40, Nk=77),
     # merge of two partial results of the FLUX-1024^2 layer (key split)
     7: Workload(7, "flux-1024-merge", "bf16", 1, 24, 4608, 128, merge=True),
+    # the Wan 2.1 inputs of workload 5 through the INT8-QK / 16-bit-PV form
+    8: Workload(5, "wan-720p-int8qk-pv16", "bf16", 1, 40, 76112, 128,
+                k_offset_var=2.0, quantised=True, pv16=True, sampled_rows=512),
 }
 
 

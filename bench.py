@@ -186,7 +186,9 @@ def main() -> int:
     tflops_kernel = flops / (ev_ms * 1e-3) / 1e12
     dkey = "int8qk" if w.quantised else w.dtype
     peak = PEAK_TFLOPS[dkey]
-    kernel_key = f"{'fa_fwd_int8qk' if w.quantised else ('fa_fwd_cross' if w.Nk else 'fa_fwd')}:{w.name}"
+    entry = ("fa_fwd_int8qk_pv16" if w.pv16 else "fa_fwd_int8qk") if w.quantised else \
+        ("fa_fwd_cross" if w.Nk else "fa_fwd")
+    kernel_key = f"{entry}:{w.name}"
     out = {
         "metric": METRIC,
         "value": round(tflops_step, 2),

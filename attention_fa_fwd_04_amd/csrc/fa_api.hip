@@ -10,6 +10,7 @@
 #include "fa.h"
 #include "fa_fwd_kernel.hpp"
 #include "fa_fwd_dma.hpp"
+#include "fa_fwd_pp.hpp"
 #include "fa_int8qk.hpp"
 #include "fa_merge.hpp"
 
@@ -93,9 +94,25 @@ struct Layouts {
 template <typename T, int D, int MASK>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
                const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
-  if constexpr (FA_USE_DMA && D == 128 && sizeof(T) == 2) {
-    // 16-bit, D = 128: K/V staged by LDS DMA, 8 waves x 128-key tiles (measured
-    // best on MI355X among 4/8 waves x 32/64/128 keys)
+#ifndef FA_USE_PP
+#define FA_USE_PP 1
+#endif
+  if constexpr (FA_USE_PP && D == 128 && sizeof(T) == 2 && MASK != fa::kMaskAdd) {
+    // 16-bit, D = 128, no score mask: the two wave groups of each SIMD
+    // alternate between the MFMA and softmax phases, 8 waves x 64-key tiles
+    using C = fa::DmaCfg<T, 64, 8>;
+    const int nqt = (Nq + C::BR - 1) / C::BR;
+    const int grid = B * H * nqt;
+    if (log_enabled())
+      std::fprintf(stderr, "[fa] fa_fwd(pp) D=%d mask=%d B=%d H=%d Nq=%d Nk=%d grid=%d block=%d BR=%d BC=64 lds=%d\n",
+                   D, MASK, B, H, Nq, Nk, grid, C::NT, C::BR, 4 * C::TILE);
+    hipLaunchKernelGGL((fa::fa_fwd_pp_kernel<T, 64, MASK>), dim3(grid), dim3(C::NT), 0, st,
+                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                       static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e);
+    return record_launch("fa_fwd_pp_kernel");
+  } else if constexpr (FA_USE_DMA && D == 128 && sizeof(T) == 2) {
+    // 16-bit, D = 128 with an additive mask: K/V staged by LDS DMA, 8 waves
+    // (measured best on MI355X among 4/8 waves x 32/64/128 keys)
 #ifndef FA_DMA_NW
 #define FA_DMA_NW 8
 #endif

@@ -89,7 +89,7 @@ def test_worked_example_fp32(dev):
     check_lse(lse, ref_l, torch.float32, "worked example")
 
 
-SWEEP_N = [1, 33, 64, 129, 1000]
+SWEEP_N = [1, 33, 64, 128, 129, 320, 1000]
 
 
 @pytest.mark.parametrize("mask_kind", ["none", "keylen", "additive"])

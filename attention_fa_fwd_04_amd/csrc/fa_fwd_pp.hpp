@@ -121,8 +121,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
 
   // DMA of kilobytes [kb0, kb0 + n) of tile j (4 rows per kilobyte) into buf;
   // the lane landing at physical chunk lane % 16 of row r fetches logical
-  // chunk (lane % 16) ^ swz(r).
-  // The row part of the offset is wave-uniform and goes in the scalar offset.
+  // chunk (lane % 16) ^ swz(r).  The whole offset is in the range-checked
+  // vector offset, so rows past n_eff read as zero.
   auto dma = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* buf, int j, int kb0, int n, bool is_v) {
     const uint32_t l = launder((uint32_t)lane);
     const uint32_t pitch = is_v ? vs : ks;
@@ -151,11 +151,6 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
   static_assert(MASK != kMaskAdd, "additive masks use fa_fwd_dma_kernel");
   const float cs = c_log2;
 
-  // ---- MFMA phase: O^T += V^T P^T for the previous tile, then S^T = K Q^T
-  // for this one.  P V runs first so the narrowed P is dead before S is
-  // produced.  Operand reads run one step ahead of the MFMAs that use them;
-  // when both halves run, the K operand reads are spread over the P V steps
-  // so they have landed by the time the Q K^T MFMAs start.
   // Lane-constant parts of the operand addresses, computed once.
   // K: row (lane % 32) of each 32-key block, chunk (2 st + lh) ^ k_swz(r)
   //    = 2 st ^ ky.

@@ -25,13 +25,17 @@
 // during the P V steps (twelve of sixteen; the last four just before the
 // MFMAs that use them) and the V operands one step ahead of their MFMAs.
 //
-// Tile traffic.  Two K and two V buffers.  Group A issues all tile DMA, at
-// the start of its softmax phase (phase 2t + 1: K(t+1) and V(t), first read
-// in phase 2t + 2; the buffers they replace, K(t-1) and V(t-2), were last
-// read by group B in phase 2t - 1), and waits for it before that phase's
-// closing barrier; group A thus never has DMA outstanding while it reads LDS.
-// The per-lane DMA offsets within a tile are computed once.  A prologue
-// loads K(0) with all eight waves.
+// Tile traffic.  Two K and two V buffers; group A loads K tiles and group B
+// V tiles, each wave a quarter, at the start of its softmax phase (which
+// reads no LDS), from per-lane offsets computed once.  Group A loads K(t+1)
+// in phase 2t + 1 (first read in phase 2t + 2; it replaces K(t-1), last read
+// in phase 2t - 1) and waits for it before that phase's closing barrier.
+// Group B loads V(t+1) in phase 2t + 2 (first read in phase 2t + 4; it
+// replaces V(t-1), last read in phase 2t + 1) and waits for it before the
+// closing barrier of phase 2t + 3; the transposing V reads of its MFMA phase
+// in between make the compiler wait for it there already, about a phase
+// after the issue.  A prologue loads K(0) with all eight waves; group B loads
+// V(0) in phase 0.
 //
 // The ragged last tile (keys [nfull BC, n_eff)) is processed first with all
 // eight waves in step, so the phase loop sees only full tiles.
@@ -305,52 +309,57 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
   auto kbuf = [&](int t) { return kbuf0 + (t & 1) * C::TILE; };
   auto vbuf = [&](int t) { return vbuf0 + (t & 1) * C::TILE; };
   if (nt > 0) {
-    const int kbA = wave * KB_B;   // group A's share (kilobytes) of each tile's DMA
-    // Per-lane byte offsets of group A's DMA share within a tile (row part
-    // of tile 0 plus swizzled chunk); a tile adds j * BC rows.
-    uint32_t koffA[KB_B], voffA[KB_B];
+    // Tile DMA: group A loads K tiles, group B loads V tiles, each wave a
+    // quarter, from per-lane offsets computed once (tile j adds j * BC rows).
+    const int kb4 = (wave & 3) * KB_B;
+    uint32_t offs[KB_B];
+    {
+      const uint32_t pitch = grp == 0 ? ks : vs;
 #pragma unroll
-    for (int i = 0; i < KB_B; ++i) {
-      const int r = (kbA + i) * 4 + (lane >> 4);
-      koffA[i] = (uint32_t)r * ks + (uint32_t)((((lane & 15) ^ k_swz(r))) << 4);
-      voffA[i] = (uint32_t)r * vs + (uint32_t)((((lane & 15) ^ v_swz(r))) << 4);
+      for (int i = 0; i < KB_B; ++i) {
+        const int r = (kb4 + i) * 4 + (lane >> 4);
+        const int sw = grp == 0 ? k_swz(r) : v_swz(r);
+        offs[i] = (uint32_t)r * pitch + (uint32_t)(((lane & 15) ^ sw) << 4);
+      }
     }
-    auto dmaA = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* buf, int j, const uint32_t* offs, uint32_t pitch) {
+    auto dma4 = [&](__amdgpu_buffer_rsrc_t rs, uint8_t* buf, int j, uint32_t pitch, const uint32_t* o) {
       const uint32_t row_off = (uint32_t)(j * BC) * pitch;
 #pragma unroll
       for (int i = 0; i < KB_B; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (kbA + i) * 1024), 16, offs[i] + row_off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (kb4 + i) * 1024), 16, o[i] + row_off, 0, 0, 0);
     };
     if (grp == 0) {
       mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{});
       lds_barrier();                                            // phase 0
       for (int t = 0; t + 1 < nt; ++t) {
-        // phase 2t + 1: load K(t + 1) and V(t), first read in phase 2t + 2;
-        // the buffers they replace, K(t - 1) and V(t - 2), were last read in
-        // phase 2t - 1
-        dmaA(kr, kbuf(t + 1), t + 1, koffA, ks);
-        dmaA(vr, vbuf(t), t, voffA, vs);
+        // phase 2t + 1: K(t + 1), first read in phase 2t + 2, replaces K(t - 1),
+        // last read in phase 2t - 1
+        dma4(kr, kbuf(t + 1), t + 1, ks, offs);
         softmax_phase(t, BoolTag<false>{});
         __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
         lds_barrier();                                          // phase 2t + 1
         mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{});
         lds_barrier();                                          // phase 2t + 2
       }
-      dmaA(vr, vbuf(nt - 1), nt - 1, voffA, vs);
       softmax_phase(nt - 1, BoolTag<false>{});
-      __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
       lds_barrier();                                            // phase 2nt - 1
       mma_phase(kbuf(0), vbuf(nt - 1), BoolTag<true>{}, BoolTag<false>{});
       lds_barrier();                                            // phase 2nt
       lds_barrier();                                            // phase 2nt + 1
     } else {
+      dma4(vr, vbuf(0), 0, vs, offs);                           // V(0), buffer unused yet
       lds_barrier();                                            // phase 0
       mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{});
+      __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): V(0) landed
       lds_barrier();                                            // phase 1
       for (int t = 0; t + 1 < nt; ++t) {
+        // phase 2t + 2: V(t + 1), first read in phase 2t + 4, replaces V(t - 1),
+        // last read in phase 2t + 1
+        dma4(vr, vbuf(t + 1), t + 1, vs, offs);
         softmax_phase(t, BoolTag<false>{});
         lds_barrier();                                          // phase 2t + 2
         mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{});
+        __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): V(t + 1) landed
         lds_barrier();                                          // phase 2t + 3
       }
       softmax_phase(nt - 1, BoolTag<false>{});

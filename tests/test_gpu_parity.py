@@ -118,6 +118,24 @@ def test_sweep(dev, dt, D, mask_kind):
         check_lse(lse, ref_l, dtype, f"N={N}")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_keylen_tile_edges(dev, dt):
+    """Key lengths on both sides of 64- and 128-key tile boundaries (tail only,
+    whole tiles with no tail, one key past a tile, zero), one per batch
+    entry, over queries that leave a partial 256-row tile."""
+    lens = [0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 1000, 1200]
+    w = Workload(96, f"tile-edges-{dt}", dt, len(lens), 2, 1200, 128)
+    inp = make_inputs(w)
+    kl = torch.tensor(lens, dtype=torch.int32)
+    say(f"case dt={dt} B={w.B} H={w.H} N={w.N} D=128 key_len={lens}")
+    o, lse = run(dev, inp, key_len=kl)
+    ref_o, ref_l = attention.naive(inp["q"].double().numpy(), inp["k"].double().numpy(),
+                                   inp["v"].double().numpy(), w.scale, key_len=np.array(lens))
+    check_o(o, ref_o, DT[dt], "key-length tile edges")
+    check_lse(lse, ref_l, DT[dt], "key-length tile edges")
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
 def test_fully_masked_rows(dev):
     w = Workload(97, "masked", "bf16", 2, 2, 100, 128)
     inp = make_inputs(w)

@@ -14,11 +14,11 @@
 #include "fa_int8qk.hpp"
 #include "fa_merge.hpp"
 
-// Tile configuration per head dimension (measured on MI355X): D = 128 runs
-// 8-wave workgroups (256 query rows) over 128-key tiles; the small head dims
-// run 4-wave workgroups over 64-key tiles; additive masks always use 64-key
-// tiles (per-score mask loads need the registers); fp32 uses 32-key tiles.
-// Every configuration keeps two waves per SIMD.
+// Tile configuration of fa_fwd_kernel (fp32, and 16-bit D = 32 / 40; 16-bit
+// D = 128 runs fa_fwd_pp_kernel or fa_fwd_dma_kernel): D = 128 (fp32) runs
+// 8-wave workgroups (256 query rows), the small head dims 4-wave workgroups
+// (128 rows) over 64-key tiles; fp32 uses 32-key tiles.  Every configuration
+// keeps two waves per SIMD.
 template <typename T, int D, int MASK> struct TileCfg {
   static constexpr int NW = (D >= 128) ? 8 : 4;
   static constexpr int BC = (sizeof(T) == 4) ? 32 : ((MASK == fa::kMaskAdd || D < 128) ? 64 : 128);
@@ -82,10 +82,6 @@ int check_common(const void* q, const void* k, const void* v, void* o, const flo
   return FA_OK;
 }
 
-#ifndef FA_USE_DMA
-#define FA_USE_DMA 1
-#endif
-
 // Row layouts of q, k, v, o in that order.
 struct Layouts {
   fa::RowLayout q, k, v, o;
@@ -94,10 +90,7 @@ struct Layouts {
 template <typename T, int D, int MASK>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
                const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
-#ifndef FA_USE_PP
-#define FA_USE_PP 1
-#endif
-  if constexpr (FA_USE_PP && D == 128 && sizeof(T) == 2 && MASK != fa::kMaskAdd) {
+  if constexpr (D == 128 && sizeof(T) == 2 && MASK != fa::kMaskAdd) {
     // 16-bit, D = 128, no score mask: the two wave groups of each SIMD
     // alternate between the MFMA and softmax phases, 8 waves x 64-key tiles
     using C = fa::DmaCfg<T, 64, 8>;
@@ -110,21 +103,11 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                        static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e);
     return record_launch("fa_fwd_pp_kernel");
-  } else if constexpr (FA_USE_DMA && D == 128 && sizeof(T) == 2) {
+  } else if constexpr (D == 128 && sizeof(T) == 2) {
     // 16-bit, D = 128 with an additive mask: K/V staged by LDS DMA, 8 waves
-    // (measured best on MI355X among 4/8 waves x 32/64/128 keys)
-#ifndef FA_DMA_NW
-#define FA_DMA_NW 8
-#endif
-#ifndef FA_DMA_BC
-#define FA_DMA_BC 128
-#endif
-#ifndef FA_DMA_MINB
-#define FA_DMA_MINB (8 / FA_DMA_NW)
-#endif
-    // additive masks load one mask value per score: 64-key tiles keep those
-    // loads within the register budget
-    constexpr int NW = FA_DMA_NW, BC = (MASK == fa::kMaskAdd) ? 64 : FA_DMA_BC, MINB = FA_DMA_MINB;
+    // in step over 64-key tiles (one mask value is loaded per score; wider
+    // tiles exceed the register budget)
+    constexpr int NW = 8, BC = 64, MINB = 1;
     using C = fa::DmaCfg<T, BC, NW>;
     const int nqt = (Nq + C::BR - 1) / C::BR;
     const int grid = B * H * nqt;

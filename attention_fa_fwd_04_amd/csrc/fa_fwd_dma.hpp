@@ -24,8 +24,10 @@
 //    operand that pairs with the lane's own scores.
 //
 // With no staging registers or LDS write instructions, each wave's tile loop
-// is only MFMA, LDS reads and the softmax arithmetic.  The default launch is
-// 8 waves (256 query rows) over 128-key tiles, four 32 KB buffers in LDS.
+// is only MFMA, LDS reads and the softmax arithmetic.  The library launches
+// this kernel for additive masks: 8 waves (256 query rows) in step over
+// 64-key tiles, four 16 KB buffers in LDS (without a score mask the same
+// staging runs in the phase-alternating schedule of fa_fwd_pp.hpp).
 #pragma once
 
 #include "fa_common.hpp"

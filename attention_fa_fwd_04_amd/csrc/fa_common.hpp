@@ -117,6 +117,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // Buffer resource over [base, base + bytes): loads at offsets outside the
 // range return zero instead of touching memory, so tails and masked rows
 // need no branches.
+// LDS destination pointer of the buffer-load-to-LDS builtin.
+typedef __attribute__((address_space(3))) void lds_void;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

@@ -59,7 +59,6 @@ __device__ __forceinline__ int k_swz(int r) { return r & 15; }
 // read is conflict-free (the previous map, 2 (r & 7), sent them to 4).
 __device__ __forceinline__ int v_swz(int r) { return ((r & 1) << 3) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1); }
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 

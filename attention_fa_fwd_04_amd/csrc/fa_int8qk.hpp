@@ -272,7 +272,9 @@ __global__ __launch_bounds__(256) void int8_v16t_kernel(
 // lane owns one query.  QK^T: v_mfma_i32_32x32x32_i8 (lane half h feeds the
 // 16 bytes of chunk 2s + h of its row, as in the 16-bit kernel).  PV:
 // v_mfma_f32_32x32x64_f8f6f4 on e4m3 operands, one instruction per 32
-// channels per 64-key tile.
+// channels per 64-key tile.  The int8 K tile and the e4m3 V^T tile reach
+// LDS by buffer-load DMA into unpadded, chunk-swizzled rows (no staging
+// registers or LDS stores; the operand reads are conflict-free).
 
 template <typename T, int MASKLEN>
 __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
@@ -281,10 +283,10 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     const int* __restrict__ key_len, T* __restrict__ O, float* __restrict__ LSE,
     int H, int N, int npad, int groups, int nqt, float c_log2) {
   constexpr int D = 128, BC = kInt8Bc, BR = 128, NT = 256;
-  constexpr int KSTR = D + 16;                  // int8 K row + pad
-  constexpr int VSTR = BC + 16;                 // e4m3 V^T row (64 keys) + pad
+  constexpr int KSTR = D;                       // int8 K row (128 bytes, chunks swizzled)
+  constexpr int VSTR = BC;                      // e4m3 V^T row (64 keys, chunks swizzled)
   constexpr int KBYTES = BC * KSTR, VBYTES = D * VSTR, BUF = KBYTES + VBYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, lh = lane >> 5;
@@ -314,25 +316,29 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   const float sq_w = sq[(size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)];
   const float* skh = sk + (size_t)bh * groups;
 
-  // staging: K tile 64 rows x 8 chunks, V^T tile 128 rows x 4 chunks -> 2 + 2 per thread
-  u32x4 kst[2], vst[2];
-  auto load_tile = [&](int j) {
+  // Tiles reach LDS by buffer-load DMA (1 KB per instruction, two K and two
+  // V instructions per wave and tile).  Rows are unpadded; the lane landing
+  // at physical chunk c of row r fetches logical chunk c ^ swz(r), K:
+  // swz = (r >> 1) & 7 (128-byte rows, two per 256-byte bank row), V^T:
+  // swz = (r >> 2) & 3 (64-byte rows, four per bank row), so the 16 rows of
+  // one 16-lane read phase fall in 16 distinct 16-byte bank groups.
+  uint32_t koff[2], voff[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int it = tid + NT * i;
-      kst[i] = buf_load16(kr, (uint32_t)(j * BC) * D + it * 16);
-      const int d = it >> 2, c = it & 3;
-      vst[i] = buf_load16(vr, (uint32_t)d * npad + j * BC + c * 16);
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int i = 0; i < 2; ++i) {
+    const int kb = wave * 2 + i;
+    const int kr_ = kb * 8 + (lane >> 3), kc = lane & 7;
+    koff[i] = (uint32_t)kr_ * D + (uint32_t)((kc ^ ((kr_ >> 1) & 7)) << 4);
+    const int vr_ = kb * 16 + (lane >> 2), vc = lane & 3;
+    voff[i] = (uint32_t)vr_ * (uint32_t)npad + (uint32_t)((vc ^ ((vr_ >> 2) & 3)) << 4);
+  }
+  auto dma_tile = [&](int j, int buf) {
     uint8_t* kb = smem + buf * BUF;
     uint8_t* vb = kb + KBYTES;
+    const uint32_t krow = (uint32_t)(j * BC) * D, vcol = (uint32_t)(j * BC);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int it = tid + NT * i;
-      *reinterpret_cast<u32x4*>(kb + (it >> 3) * KSTR + (it & 7) * 16) = kst[i];
-      *reinterpret_cast<u32x4*>(vb + (it >> 2) * VSTR + (it & 3) * 16) = vst[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kb + (wave * 2 + i) * 1024), 16, koff[i] + krow, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vb + (wave * 2 + i) * 1024), 16, voff[i] + vcol, 0, 0, 0);
     }
   };
 
@@ -347,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   auto step = [&](int j, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int buf = j & 1;
-    load_tile(j + 1);
+    dma_tile(j + 1, buf ^ 1);                     // past the last tile: never read
     const uint8_t* kb = smem + buf * BUF;
     const uint8_t* vb = kb + KBYTES;
     const int kv0 = j * BC;
@@ -360,7 +366,8 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
       for (int i = 0; i < 16; ++i) si[G][i] = 0;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * G + ln) * KSTR + (2 * st + lh) * 16);
+        const int r = 32 * G + ln;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + r * KSTR + ((((2 * st + lh) ^ ((r >> 1) & 7))) << 4));
         si[G] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
                                                       __builtin_bit_cast(i32x4, qreg[st]), si[G], 0, 0, 0);
       }
@@ -427,19 +434,20 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
                        (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint8_t* vrow = vb + (32 * p + ln) * VSTR + 32 * lh;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(vrow);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(vrow + 16);
+      const int r = 32 * p + ln, sw = (r >> 2) & 3;
+      const uint8_t* vrow = vb + r * VSTR;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(vrow + (((2 * lh) ^ sw) << 4));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(vrow + (((2 * lh + 1) ^ sw) << 4));
       const i32x8 aop = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       acc[p] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[p], 0, 0, 0, 0, 0, 0);
     }
-    store_tile(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): tile j + 1 landed
     __syncthreads();
   };
 
-  load_tile(0);
-  store_tile(0);
+  dma_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   const int nfull = n_eff / BC;
   for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});

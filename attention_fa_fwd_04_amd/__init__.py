@@ -23,7 +23,8 @@ FA_MASK_NONE, FA_MASK_ADDITIVE, FA_MASK_KEYLEN = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
 FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
 
-EXPORTED = ("fa_fwd", "fa_fwd_cross", "fa_fwd_strided", "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk",
+EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_fwd_cross", "fa_fwd_strided",
+            "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk",
             "fa_fwd_int8qk_pv16_workspace_bytes", "fa_fwd_int8qk_pv16",
             "fa_merge", "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
@@ -69,6 +70,10 @@ def lib() -> ctypes.CDLL:
     mp = ctypes.POINTER(fa_mask_t)
     h.fa_fwd.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp]
     h.fa_fwd.restype = i32
+    h.fa_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    h.fa_fwd_workspace_bytes.restype = sz
+    h.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    h.fa_fwd_ws.restype = i32
     h.fa_fwd_cross.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, i32, f32, i32, vp]
     h.fa_fwd_cross.restype = i32
     sp = ctypes.POINTER(fa_stride_t)
@@ -100,6 +105,16 @@ def lib() -> ctypes.CDLL:
 
 def fa_fwd(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream) -> int:
     return lib().fa_fwd(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream)
+
+
+def fa_fwd_workspace_bytes(B, H, N, D, dtype) -> int:
+    return lib().fa_fwd_workspace_bytes(B, H, N, D, dtype)
+
+
+def fa_fwd_ws(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace, workspace_bytes,
+              hip_stream) -> int:
+    return lib().fa_fwd_ws(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace,
+                           workspace_bytes, hip_stream)
 
 
 def fa_fwd_cross(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, hip_stream) -> int:
@@ -215,13 +230,35 @@ def _mask_struct(q, attn_mask, key_len, keep, nk=None):
     return None
 
 
+# Zero-filled workspaces of fa_fwd_ws, one per (device, stream): the arrival
+# counters at their start return to zero after every completed call, so each
+# is zero-filled once and reused by the calls queued on its stream.
+_split_ws = {}
+
+
+def split_workspace(device, stream, nbytes: int):
+    """The cached fa_fwd_ws workspace for (device, stream), at least nbytes."""
+    import torch
+    key = (device.index, stream)
+    ws = _split_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("fa_fwd_ws needs its workspace before graph capture: run the call "
+                               "once eagerly on the capture stream first")
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _split_ws[key] = ws
+    return ws
+
+
 def fwd(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
-        return_lse: bool = False, out=None):
+        return_lse: bool = False, out=None, split: bool = True):
     """O = softmax(scale * q k^T + mask) v for GPU tensors q [B, H, Nq, D] and
     k, v [B, H, Nk, D] (self-attention when Nq == Nk, else cross-attention).
     The tensors may be strided views with contiguous D (e.g. [B, N, H, D]
     projections viewed through .transpose(1, 2)); those go through
-    fa_fwd_strided without a copy.  O has q's layout unless `out` is given."""
+    fa_fwd_strided without a copy.  O has q's layout unless `out` is given.
+    Contiguous unmasked self-attention goes through fa_fwd_ws (the even
+    key-tile split) when the shape takes it, unless split=False."""
     import torch
     _check_qkv(q, k, v, same_length=False, strided=True)
     B, H, Nq, D = q.shape
@@ -242,9 +279,16 @@ def fwd(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
                             B, H, Nq, Nk, D, *[ctypes.byref(x) for x in sd], scale, _dtype_code(q), st)
         where = "fa_fwd_strided"
     elif Nq == Nk:
-        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lp, mp,
-                    B, H, Nq, D, scale, _dtype_code(q), st)
-        where = "fa_fwd"
+        need = fa_fwd_workspace_bytes(B, H, Nq, D, _dtype_code(q)) if split and m is None else 0
+        if need > 0:
+            ws = split_workspace(q.device, st, need)
+            rc = fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lp, mp,
+                           B, H, Nq, D, scale, _dtype_code(q), ws.data_ptr(), ws.numel(), st)
+            where = "fa_fwd_ws"
+        else:
+            rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lp, mp,
+                        B, H, Nq, D, scale, _dtype_code(q), st)
+            where = "fa_fwd"
     else:
         rc = fa_fwd_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lp, mp,
                           B, H, Nq, Nk, D, scale, _dtype_code(q), st)

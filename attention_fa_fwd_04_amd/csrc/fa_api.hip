@@ -2,6 +2,7 @@
 // Declarations and conventions: include/fa.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -99,9 +100,10 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     if (log_enabled())
       std::fprintf(stderr, "[fa] fa_fwd(pp) D=%d mask=%d B=%d H=%d Nq=%d Nk=%d grid=%d block=%d BR=%d BC=64 lds=%d\n",
                    D, MASK, B, H, Nq, Nk, grid, C::NT, C::BR, 4 * C::TILE);
-    hipLaunchKernelGGL((fa::fa_fwd_pp_kernel<T, 64, MASK>), dim3(grid), dim3(C::NT), 0, st,
+    hipLaunchKernelGGL((fa::fa_fwd_pp_kernel<T, 64, MASK, false>), dim3(grid), dim3(C::NT), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                       static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e);
+                       static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e,
+                       fa::SplitArgs{nullptr, nullptr, 0, 0});
     return record_launch("fa_fwd_pp_kernel");
   } else if constexpr (D == 128 && sizeof(T) == 2) {
     // 16-bit, D = 128 with an additive mask: K/V staged by LDS DMA, 8 waves
@@ -209,6 +211,75 @@ int contiguous_range_ok(int Nq, int Nk, int D, int dt) {
   return (int64_t)(Nq + kRowMargin) * D * e <= (int64_t)UINT32_MAX &&
          (int64_t)(Nk + kRowMargin) * D * e <= (int64_t)UINT32_MAX;
 }
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// The even key-tile split of fa_fwd_pp_kernel (16-bit, D = 128, no mask,
+// N a multiple of the 64-key tile): one workgroup per CU, used when whole
+// query blocks would fill the last round of workgroups to less than 90 % and
+// every workgroup still covers at least one block's worth of tiles (so a
+// block is split at most once).
+struct SplitPlan {
+  int grid = 0;           // 0: the plain launch
+  int nqt = 0, tiles = 0;
+  int64_t units = 0;
+  size_t bytes = 0;       // workspace
+};
+constexpr int kSplitBR = 256, kSplitBC = 64;
+
+SplitPlan split_plan(int B, int H, int N, int D, int dtype, int mask_kind) {
+  SplitPlan p;
+  if ((dtype != FA_F16 && dtype != FA_BF16) || D != 128 || mask_kind != FA_MASK_NONE) return p;
+  if (B <= 0 || H <= 0 || N <= 0 || N % kSplitBC != 0) return p;
+  const int G = cu_count();
+  if (G <= 0) return p;
+  const int nqt = (N + kSplitBR - 1) / kSplitBR;
+  const int64_t jobs = (int64_t)B * H * nqt;
+  if (jobs < G) return p;
+  const int64_t rounds = (jobs + G - 1) / G;
+  if (jobs * 10 >= rounds * G * 9) return p;   // the last round is >= 90 % full
+  p.grid = G;
+  p.nqt = nqt;
+  p.tiles = (N + kSplitBC - 1) / kSplitBC;
+  p.units = jobs * p.tiles;
+  // segments per workgroup: whole blocks of its range plus two split parts
+  if ((p.units + G - 1) / G / p.tiles + 3 > fa::kMaxSegments) return SplitPlan{};
+  const size_t cnt_bytes = ((size_t)(G + 1) * sizeof(unsigned) + 255) / 256 * 256;
+  p.bytes = cnt_bytes + (size_t)(G + 1) * 2 * fa::kPartFloats * sizeof(float);
+  return p;
+}
+
+template <typename T>
+int launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                 float scale, const SplitPlan& p, void* workspace, hipStream_t st) {
+  using C = fa::DmaCfg<T, kSplitBC, 8>;
+  static_assert(C::BR == kSplitBR, "query block of the split launch");
+  const Layouts L = contiguous_layouts(H, N, N, 128);
+  const size_t cnt_bytes = ((size_t)(p.grid + 1) * sizeof(unsigned) + 255) / 256 * 256;
+  fa::SplitArgs sk{static_cast<unsigned*>(workspace),
+                   reinterpret_cast<float*>(static_cast<char*>(workspace) + cnt_bytes), p.units, p.tiles};
+  if (log_enabled())
+    std::fprintf(stderr, "[fa] fa_fwd_ws(pp, split) B=%d H=%d N=%d blocks=%lld tiles=%d grid=%d ws=%zu\n",
+                 B, H, N, (long long)B * H * p.nqt, p.tiles, p.grid, p.bytes);
+  const fa::MaskArgs m{nullptr, 0, 0, 0, 0};
+  hipLaunchKernelGGL((fa::fa_fwd_pp_kernel<T, kSplitBC, fa::kMaskNone, true>), dim3(p.grid), dim3(C::NT), 0, st,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                     static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, N, N, p.nqt, scale * fa::kLog2e, sk);
+  return record_launch("fa_fwd_pp_kernel(split)");
+}
 }  // namespace
 
 extern "C" {
@@ -243,6 +314,27 @@ FA_API int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, 
   auto rl = [](const fa_stride_t* s) { return fa::RowLayout{s->stride_b, s->stride_h, s->stride_n}; };
   const Layouts L{rl(q_strides), rl(k_strides), rl(v_strides), rl(o_strides)};
   return fwd_common(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, L, hip_stream);
+}
+
+FA_API size_t fa_fwd_workspace_bytes(int B, int H, int N, int D, fa_dtype_t dtype) {
+  return split_plan(B, H, N, D, dtype, FA_MASK_NONE).bytes;
+}
+
+FA_API int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                     fa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const int kind = mask ? mask->kind : FA_MASK_NONE;
+  const SplitPlan p = split_plan(B, H, N, D, dtype, kind);
+  if (p.grid == 0)
+    return fa_fwd(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream);
+  int rc = check_common(q, k, v, o, lse, mask, B, H, N, D, scale);
+  if (rc != FA_OK) return rc;
+  if (!contiguous_range_ok(N, N, D, dtype)) return FA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < p.bytes) return FA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (dtype == FA_BF16) return launch_split<__bf16>(q, k, v, o, lse, B, H, N, scale, p, workspace, st);
+  return launch_split<_Float16>(q, k, v, o, lse, B, H, N, scale, p, workspace, st);
 }
 
 FA_API size_t fa_fwd_int8qk_workspace_bytes(int B, int H, int N, int D) {
@@ -369,6 +461,6 @@ FA_API const char* fa_status_string(int status) {
 
 FA_API const char* fa_last_hip_error(void) { return g_hip_err; }
 
-FA_API int fa_abi_version(void) { return 1; }
+FA_API int fa_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -44,6 +44,23 @@
 // them).  With the lazy rescale the hot path only compares each half's max
 // with the shared running max; the halves are combined only when some row
 // crosses the threshold, and once at the end for the denominator.
+//
+// Even split of the key tiles (SPLIT = true, no mask).  When the number of
+// query blocks is not close to a multiple of the CU count, the last round
+// of workgroups leaves CUs idle (432 blocks of 256 rows on 256 CUs run in
+// two rounds, the second 69 % full).  The split launch runs one workgroup
+// per CU and hands each the same number of (query block, key tile) units in
+// block-major order, so a workgroup finishes the key tiles of a block its
+// predecessor started, takes whole blocks, and starts a block its successor
+// finishes.  A block split between two workgroups is the same online
+// softmax over two disjoint key ranges: each part leaves its unnormalised
+// accumulator, running max and denominator in the workspace, and the part
+// that arrives second (an arrival counter per split) combines the two by
+// the handbook's rescale, exp(m_part - m), and stores O and lse.  The
+// combination is written as a function of (first-range part, second-range
+// part) whichever arrives last, so the result does not depend on arrival
+// order.  Both split parts of a workgroup run before its whole blocks, so
+// the combining traffic overlaps other workgroups' compute.
 #pragma once
 
 #include "fa_common.hpp"
@@ -68,6 +85,23 @@ __device__ __forceinline__ uint32_t launder(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+// Workspace of the split launch.  cnt[s] counts the parts of split s that
+// have arrived; it returns to zero when the second one arrives, so a
+// workspace that starts zeroed stays zeroed between calls.
+struct SplitArgs {
+  unsigned* cnt;    // [grid + 1]
+  float* part;      // [grid + 1][2][kPartFloats]
+  int64_t units;    // query blocks x key tiles per block
+  int tiles;        // key tiles per query block
+};
+// One part: 8 waves x 16 four-float accumulator chunks x 64 lanes, then
+// (running max, denominator) per lane.
+constexpr int kPartAccFloats = 8 * 16 * 64 * 4;
+constexpr int kPartFloats = kPartAccFloats + 8 * 64 * 2;
+// Segments of one workgroup of the split launch: at most two split parts
+// plus the whole blocks of its range (the host keeps this bound).
+constexpr int kMaxSegments = 16;
+
 // Workgroup barrier that orders LDS accesses (compiler and hardware) but,
 // unlike __syncthreads(), does not wait for outstanding DMA.
 __device__ __forceinline__ void lds_barrier() {
@@ -76,12 +110,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename T, int BC, int MASK>
+template <typename T, int BC, int MASK, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, MaskArgs mask,
     RowLayout lq, RowLayout lk, RowLayout lv, RowLayout lo,
-    int H, int Nq, int Nk, int nqt, float c_log2) {
+    int H, int Nq, int Nk, int nqt, float c_log2, SplitArgs sk) {
   constexpr int NW = 8;
   using C = DmaCfg<T, BC, NW>;
   constexpr int D = C::D, SB = C::SB, QKS = C::QKS, PVB = C::PVB;
@@ -90,6 +124,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
   constexpr int KB_B = KB_PER_TILE / 4;                // per wave when one group of four loads
   static_assert(KB_PER_TILE % NW == 0, "tile must split over 8 waves");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];   // K0 K1 V0 V1
+  __shared__ unsigned arrival;
+  static_assert(!SPLIT || MASK == kMaskNone, "the split launch takes no mask");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -98,19 +134,73 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
   const int ln = lane & 31, lh = lane >> 5;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nqt, qt = logical - bh * nqt;
-  const int b = bh / H, h = bh - b * H;
-  const uint32_t qs = (uint32_t)(lq.sn * 2), ks = (uint32_t)(lk.sn * 2), vs = (uint32_t)(lv.sn * 2);
+  // The split launch takes contiguous [B, H, N, 128] tensors only, so its
+  // row pitches are constants (fewer scalar registers live across segments).
+  const uint32_t qs = SPLIT ? 2u * D : (uint32_t)(lq.sn * 2);
+  const uint32_t ks = SPLIT ? 2u * D : (uint32_t)(lk.sn * 2);
+  const uint32_t vs = SPLIT ? 2u * D : (uint32_t)(lv.sn * 2);
 
-  int n_eff = Nk;
+  // Segments: (query block, key tiles [t0, t1)).  Without the split, one
+  // segment: the whole key range of block `logical`.  With it, units
+  // [u0, u1) of the block-major (block, tile) order: the first part of the
+  // block containing u1 (if u1 falls inside one), the second part of the
+  // block containing u0 (if u0 falls inside one), then the whole blocks.
+  // The split launch lists its segments in LDS once (job, t0, t1, part,
+  // slot), so nothing but the segment index stays live across them.
+  __shared__ int segd[kMaxSegments][5];
+  __shared__ int nseg_s;
+  if constexpr (SPLIT) {
+    if (tid == 0) {
+      const int64_t G = gridDim.x, TT = sk.tiles;
+      const int64_t u0 = (int64_t)logical * sk.units / G;
+      const int64_t u1 = ((int64_t)logical + 1) * sk.units / G;
+      int n = 0;
+      auto put = [&](int64_t job, int64_t t0, int64_t t1, int part, int slot) {
+        if (n < kMaxSegments) {
+          segd[n][0] = (int)job; segd[n][1] = (int)t0; segd[n][2] = (int)t1; segd[n][3] = part; segd[n][4] = slot;
+        }
+        ++n;
+      };
+      if (u1 % TT != 0) put(u1 / TT, 0, u1 % TT, 0, logical + 1);
+      if (u0 % TT != 0) put(u0 / TT, u0 % TT, TT, 1, logical);
+      for (int64_t j = (u0 + TT - 1) / TT; j < u1 / TT; ++j) put(j, 0, TT, -1, 0);
+      nseg_s = n < kMaxSegments ? n : kMaxSegments;
+    }
+    __syncthreads();
+  }
+  // One segment: query block `job`, key tiles [t0, t1) (t1 ignored without
+  // the split); part 0 / 1 is the first / second key range of split `slot`,
+  // -1 a whole block.
+  auto segment = [&](const int job, const int t0, const int t1, const int part, const int slot) {
+  const int bh = job / nqt, qt = job - bh * nqt;
+  const int b = bh / H, h = bh - b * H;
+
+  int n_all = Nk;
   if constexpr (MASK == kMaskLen) {
     const int L = reinterpret_cast<const int*>(mask.ptr)[b];
-    n_eff = L < 0 ? 0 : (L > Nk ? Nk : L);
+    n_all = L < 0 ? 0 : (L > Nk ? Nk : L);
+  }
+  // keys [k0, k0 + n_eff) of this segment; the K and V ranges start at k0
+  int k0 = 0, n_eff = n_all;
+  if constexpr (SPLIT) {
+    k0 = t0 * BC;
+    n_eff = (t1 >= sk.tiles ? n_all : t1 * BC) - k0;
   }
   const int ntiles = (n_eff + BC - 1) / BC;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + b * lq.sb + h * lq.sh, (uint32_t)Nq * qs);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + b * lk.sb + h * lk.sh, (uint32_t)n_eff * ks);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + b * lv.sb + h * lv.sh, (uint32_t)n_eff * vs);
+  const T* qh = Q + b * lq.sb + h * lq.sh;
+  const T* kh = K + b * lk.sb + h * lk.sh;
+  const T* vh = V + b * lv.sb + h * lv.sh;
+  T* oh = O + b * lo.sb + h * lo.sh;
+  if constexpr (SPLIT) {
+    const int64_t ho = (int64_t)bh * Nq * D;
+    qh = Q + ho;
+    kh = K + ho + (int64_t)k0 * D;
+    vh = V + ho + (int64_t)k0 * D;
+    oh = O + ho;
+  }
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (uint32_t)Nq * qs);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh, (uint32_t)n_eff * ks);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh, (uint32_t)n_eff * vs);
 
   const int q_row = qt * C::BR + wave * 32 + ln;
   const bool q_ok = q_row < Nq;
@@ -287,7 +377,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
   // phase loop, with all eight waves in step; the loop then only sees full
   // tiles.  The order of key tiles does not change the result beyond rounding.
   const int nfull = n_eff / BC;
-  if (nfull < ntiles) {
+  if (!SPLIT && nfull < ntiles) {             // the split launch needs N % BC == 0
     dma(kr, kbuf0, nfull, wave * KB_ALL, KB_ALL, false);
     dma(vr, vbuf0, nfull, wave * KB_ALL, KB_ALL, true);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -369,10 +459,70 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
     }
   }
 
-  const float l_tot = wave_sum_halves(l_run);
+  float l_tot = wave_sum_halves(l_run);
+  float m_fin = m_run;
+  if constexpr (SPLIT) {
+    if (part >= 0) {
+      // Leave this part, count it, and combine if the other part is in.
+      // The two parts may run on different XCDs (separate L2s): partials
+      // are written through and read back at device scope (the sc1 cache
+      // policy) instead of fencing, which would write back and invalidate
+      // the whole L2 and with it the K/V tiles other workgroups reuse.
+      constexpr int kDeviceScope = 16;          // sc1
+      const __amdgpu_buffer_rsrc_t pr =
+          make_rsrc(sk.part, (uint32_t)((gridDim.x + 1) * 2 * (uint32_t)kPartFloats * 4u));
+      const uint32_t mine = (uint32_t)(slot * 2 + part) * (uint32_t)kPartFloats * 4u;
+      const uint32_t other = (uint32_t)(slot * 2 + (1 - part)) * (uint32_t)kPartFloats * 4u;
+      const uint32_t lane_acc = (uint32_t)(wave * 16 * 64 + lane) * 16u;
+      const uint32_t lane_ml = (uint32_t)kPartAccFloats * 4u + (uint32_t)(wave * 64 + lane) * 8u;
+#pragma unroll
+      for (int p = 0; p < PVB; ++p)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = {acc[p][4 * g], acc[p][4 * g + 1], acc[p][4 * g + 2], acc[p][4 * g + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), pr,
+                                                 (int)(mine + lane_acc + (4 * p + g) * 64 * 16), 0, kDeviceScope);
+        }
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{m_run, l_tot}), pr,
+                                            (int)(mine + lane_ml), 0, kDeviceScope);
+      __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's part is written
+      __syncthreads();
+      if (tid == 0) arrival = atomicInc(sk.cnt + slot, 1u);
+      __syncthreads();
+      if (arrival == 0) return;                 // first to arrive: the other part stores
+      f32x4 po[PVB * 4];
+#pragma unroll
+      for (int c = 0; c < PVB * 4; ++c)
+        po[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              pr, (int)(other + lane_acc + c * 64 * 16), 0, kDeviceScope));
+      const f32x2 ml = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                    pr, (int)(other + lane_ml), 0, kDeviceScope));
+      // (first-range part, second-range part) whichever this is
+      const bool first = part == 0;
+      const float ma = first ? m_run : ml.x, mb = first ? ml.x : m_run;
+      const float la = first ? l_tot : ml.y, lb = first ? ml.y : l_tot;
+      const float mm = fmaxf(ma, mb);
+      const float ref = mm == -INFINITY ? 0.f : mm;
+      const float wa = __builtin_amdgcn_exp2f(ma - ref), wb = __builtin_amdgcn_exp2f(mb - ref);
+#pragma unroll
+      for (int p = 0; p < PVB; ++p)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = po[4 * p + g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float own = acc[p][4 * g + e];
+            const float a = first ? own : x[e], bb = first ? x[e] : own;
+            acc[p][4 * g + e] = a * wa + bb * wb;
+          }
+        }
+      l_tot = la * wa + lb * wb;
+      m_fin = mm;
+    }
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q_ok) {
-    T* orow = O + b * lo.sb + h * lo.sh + (int64_t)q_row * lo.sn;
+    T* orow = oh + (int64_t)q_row * (SPLIT ? D : lo.sn);
 #pragma unroll
     for (int p = 0; p < PVB; ++p)
 #pragma unroll
@@ -382,7 +532,18 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
                   acc[p][4 * g + 2] * inv, acc[p][4 * g + 3] * inv);
       }
     if (LSE != nullptr && lh == 0)
-      LSE[(size_t)bh * Nq + q_row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      LSE[(size_t)bh * Nq + q_row] = l_tot > 0.f ? (m_fin + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+  };
+
+  if constexpr (SPLIT) {
+    const int nseg = __builtin_amdgcn_readfirstlane(nseg_s);
+    for (int seg = 0; seg < nseg; ++seg)
+      segment(__builtin_amdgcn_readfirstlane(segd[seg][0]), __builtin_amdgcn_readfirstlane(segd[seg][1]),
+              __builtin_amdgcn_readfirstlane(segd[seg][2]), __builtin_amdgcn_readfirstlane(segd[seg][3]),
+              __builtin_amdgcn_readfirstlane(segd[seg][4]));
+  } else {
+    segment(logical, 0, 0, -1, 0);
   }
 }
 

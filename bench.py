@@ -131,7 +131,7 @@ def main() -> int:
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall / steps * 1e3
 
-    def measure(w, steps, warmup):
+    def measure(w, steps, warmup, split=True):
         if w.merge:
             # two partial results of the layer (seeded) merged into a third buffer
             g = torch.Generator(device="cpu").manual_seed(w.wid)
@@ -150,7 +150,7 @@ def main() -> int:
             pv = "16" if w.pv16 else "fp8"
             call = lambda: fa.fwd_int8qk(q, k, v, key_len=kl, workspace=ws, out=o, pv=pv)  # noqa: E731
         else:
-            call = lambda: fa.fwd(q, k, v, key_len=kl, out=o)  # noqa: E731
+            call = lambda: fa.fwd(q, k, v, key_len=kl, out=o, split=split)  # noqa: E731
         return timed(call, steps, warmup)
 
     def merge_bytes(w):
@@ -186,8 +186,10 @@ def main() -> int:
     tflops_kernel = flops / (ev_ms * 1e-3) / 1e12
     dkey = "int8qk" if w.quantised else w.dtype
     peak = PEAK_TFLOPS[dkey]
+    split = (not w.quantised and not w.Nk and not w.key_len and w.dtype != "f32" and
+             fa.fa_fwd_workspace_bytes(w.B, w.H, w.N, w.D, fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F16) > 0)
     entry = ("fa_fwd_int8qk_pv16" if w.pv16 else "fa_fwd_int8qk") if w.quantised else \
-        ("fa_fwd_cross" if w.Nk else "fa_fwd")
+        ("fa_fwd_cross" if w.Nk else ("fa_fwd_ws" if split else "fa_fwd"))
     kernel_key = f"{entry}:{w.name}"
     out = {
         "metric": METRIC,
@@ -203,7 +205,7 @@ def main() -> int:
         "dtype": "int8/fp8 (bf16 in/out)" if w.quantised else w.dtype,
         "data": "synthetic (seeded N(0,1) tensors of the workload's shape)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "Nk": w.n_keys, "D": w.D,
-                   "mask": "key_len" if w.key_len else "none", "causal": False},
+                   "mask": "key_len" if w.key_len else "none", "causal": False, "entry": entry},
         "roofline": {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops_kernel / peak, 4),
                      "traffic": traffic_for(kernel_key)},
@@ -220,6 +222,9 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(w)
     if args.extra:
         extra = {}
+        if split:
+            u_ms, _ = measure(w, 20, 3, split=False)
+            extra[w.name + " (fa_fwd, no split)"] = {"ms": round(u_ms, 4), "tflops": round(flops / (u_ms * 1e-3) / 1e12, 2)}
         for wid in (3, 4, 5, 6, 7):
             wx = WORKLOADS[wid]
             if wx.merge:

@@ -24,7 +24,8 @@
  *     error nothing is launched and a negative FA_ERR_* code is returned.
  *   - A row whose every key is masked yields O = 0 and lse = -inf.
  *   - Output is bitwise deterministic for identical inputs and launch
- *     configuration (fixed reduction order, no atomics).
+ *     configuration (fixed reduction order; the only atomic, in fa_fwd_ws,
+ *     counts arrivals and does not order any arithmetic).
  */
 #ifndef FA_H
 #define FA_H
@@ -127,6 +128,38 @@ FA_API int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, 
                           const fa_stride_t* q_strides, const fa_stride_t* k_strides,
                           const fa_stride_t* v_strides, const fa_stride_t* o_strides,
                           float scale, fa_dtype_t dtype, void* hip_stream);
+
+/*
+ * fa_fwd with an even split of the key tiles over the compute units, for
+ * shapes whose query blocks (256 rows) would leave the last round of
+ * workgroups under 90 % full (e.g. B=1, H=24, N=4608: 432 blocks on 256
+ * CUs).  One workgroup per CU takes an equal share of the (query block, key
+ * tile) pairs; a block whose keys fall in two shares is computed as two
+ * online softmaxes over disjoint key ranges whose unnormalised accumulators,
+ * running maxima and denominators are combined by the handbook's rescale
+ * (section "注意力：从 O(N²) 显存到分块": exp(m_old - m_new) on both the
+ * accumulator and the denominator) by whichever part finishes second.  The
+ * combination is a fixed function of (first key range, second key range),
+ * so results are bitwise deterministic; they differ from fa_fwd's only by
+ * rounding (a different summation order over the keys of split blocks).
+ *   fa_fwd_workspace_bytes(B,H,N,D,dtype): bytes the split needs on the
+ *     CURRENT device (it depends on the CU count), or 0 when the shape does
+ *     not take the split: then fa_fwd_ws is fa_fwd and ignores workspace.
+ *     The split is taken for dtype F16/BF16, D = 128, no mask (NULL or
+ *     FA_MASK_NONE), N a multiple of 64, at least one query block per CU.
+ *   workspace: 256-byte aligned device memory of at least that size, all
+ *     zero before its first use.  It begins with one arrival counter per
+ *     split, and every completed call leaves the counters at zero again, so
+ *     a workspace is zero-filled once and reused; the rest is scratch for
+ *     partial results.  Calls that share a workspace must be ordered on one
+ *     stream (concurrent calls would race on the counters).
+ * Everything else as fa_fwd.  Errors: FA_ERR_WORKSPACE if the split is taken
+ * and workspace is NULL or too small, FA_ERR_ALIGN if it is misaligned.
+ */
+FA_API size_t fa_fwd_workspace_bytes(int B, int H, int N, int D, fa_dtype_t dtype);
+FA_API int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                     fa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * INT8-QK / FP8-PV variant (handbook page, section "SageAttention").  Steps:

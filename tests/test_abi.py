@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_static_queries(lib):
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
     assert fa.fa_int8qk_kv_block() % 64 == 0
     assert fa.fa_status_string(0) == "ok"
     for code in range(-7, 0):

@@ -1,0 +1,209 @@
+"""fa_fwd_ws: the even split of key tiles over the compute units.
+
+Shapes whose 256-row query blocks leave the last round of workgroups under
+90 % full take the split (one workgroup per CU, blocks straddling two shares
+computed as two partial online softmaxes and combined).  The tests compare it
+element by element with the CPU oracle and with the unsplit kernel, check that
+it is bitwise deterministic, that its arrival counters are back at zero after
+each call (the workspace is reused), that a graph replays it, and that shapes
+outside its domain fall back to fa_fwd.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_fa_fwd_04_amd as fa
+from attention_fa_fwd_04_amd.workloads import WORKLOADS, make_inputs
+from oracle import attention
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    fa.lib()
+    return torch.device("cuda", 0)
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def n_cu(dev):
+    return torch.cuda.get_device_properties(dev).multi_processor_count
+
+
+def blocks(B, H, N):
+    return B * H * ((N + 255) // 256)
+
+
+def takes_split(dev, B, H, N):
+    G = n_cu(dev)
+    J = blocks(B, H, N)
+    rounds = (J + G - 1) // G
+    return N % 64 == 0 and J >= G and J * 10 < rounds * G * 9
+
+
+def call_ws(q, k, v, o, lse, ws, scale, dt=fa.FA_BF16):
+    B, H, N, D = q.shape
+    return fa.fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        lse.data_ptr() if lse is not None else None, None, B, H, N, D, scale, dt,
+                        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                        torch.cuda.current_stream().cuda_stream)
+
+
+def counters_zero(ws, G):
+    return bool(torch.all(ws[:4 * (G + 1)] == 0).item())
+
+
+# (B, H, N): FLUX-shaped heads at reduced sizes with different numbers of
+# blocks per CU, so the split points fall at different key tiles
+SHAPES = [(1, 18, 4096), (2, 5, 8192), (1, 40, 1792), (3, 7, 3328)]
+
+
+@pytest.mark.parametrize("B,H,N", SHAPES)
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_split_matches_oracle_and_unsplit(dev, B, H, N, dt):
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    code = {"bf16": fa.FA_BF16, "f16": fa.FA_F16}[dt]
+    assert takes_split(dev, B, H, N), "shape chosen to take the split"
+    need = fa.fa_fwd_workspace_bytes(B, H, N, 128, code)
+    assert need > 0
+    w = WORKLOADS[2].with_shape(B=B, H=H, N=N)
+    say(f"case split {dt} B={B} H={H} N={N} blocks={blocks(B, H, N)} CUs={n_cu(dev)} ws={need}")
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev).to(tdt) for n in ("q", "k", "v"))
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    assert call_ws(q, k, v, o, lse, ws, w.scale, code) == 0
+    torch.cuda.synchronize()
+    assert counters_zero(ws, n_cu(dev))
+    o_plain, lse_plain = fa.fwd(q, k, v, return_lse=True, split=False)
+    torch.cuda.synchronize()
+    # the oracle on the same rounded inputs, every element of every head
+    qd, kd, vd = (t.cpu().double().numpy() for t in (q, k, v))
+    err, lerr = [], []
+    for b in range(B):
+        for h in range(H):
+            ro, rl = attention.naive(qd[b:b + 1, h:h + 1], kd[b:b + 1, h:h + 1], vd[b:b + 1, h:h + 1], w.scale)
+            err.append(np.abs(o[b, h].cpu().double().numpy() - ro[0, 0]).ravel())
+            lerr.append(np.abs(lse[b, h].cpu().double().numpy() - rl[0, 0]).ravel())
+    err = np.concatenate(err)
+    lerr = np.concatenate(lerr)
+    d_plain = (o.float() - o_plain.float()).abs().max().item()
+    say(f"  max|err|={err.max():.3e} mean|err|={err.mean():.3e} lse={lerr.max():.3e} "
+        f"vs unsplit max={d_plain:.3e}")
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3
+    assert lerr.max() <= 1e-4
+    # the unsplit kernel differs only by summation order over split blocks
+    assert d_plain <= 1e-2
+    assert (lse - lse_plain).abs().max().item() <= 1e-4
+
+
+def test_split_deterministic_and_counters_reset(dev):
+    B, H, N = 1, 24, 4608                      # the FLUX-1024 shape
+    assert takes_split(dev, B, H, N)
+    w = WORKLOADS[2]
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    need = fa.fa_fwd_workspace_bytes(B, H, N, 128, fa.FA_BF16)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    outs = []
+    for i in range(4):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        assert call_ws(q, k, v, o, lse, ws, w.scale) == 0
+        torch.cuda.synchronize()
+        assert counters_zero(ws, n_cu(dev)), f"call {i}"
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), outs[0][1].view(torch.int32))
+    # without lse, the same O
+    o = torch.empty_like(q)
+    assert call_ws(q, k, v, o, None, ws, w.scale) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+
+
+def test_split_guard_bands(dev):
+    """Nothing is written outside o, lse and the workspace."""
+    B, H, N = 2, 5, 8192
+    w = WORKLOADS[2].with_shape(B=B, H=H, N=N)
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    need = fa.fa_fwd_workspace_bytes(B, H, N, 128, fa.FA_BF16)
+    G = 65536
+    og = torch.full((G + q.numel() + G,), 7.0, dtype=q.dtype, device=dev)
+    lg = torch.full((G + B * H * N + G,), 7.0, dtype=torch.float32, device=dev)
+    wg = torch.full((G + need + G,), 0x5A, dtype=torch.uint8, device=dev)
+    wg[G:G + need].zero_()
+    o = og[G:G + q.numel()].view(q.shape)
+    lse = lg[G:G + B * H * N].view(B, H, N)
+    ws = wg[G:G + need]
+    assert call_ws(q, k, v, o, lse, ws, w.scale) == 0
+    torch.cuda.synchronize()
+    assert torch.all(og[:G] == 7) and torch.all(og[-G:] == 7)
+    assert torch.all(lg[:G] == 7) and torch.all(lg[-G:] == 7)
+    assert torch.all(wg[:G] == 0x5A) and torch.all(wg[-G:] == 0x5A)
+    ref = fa.fwd(q, k, v, split=False)
+    torch.cuda.synchronize()
+    assert (o.float() - ref.float()).abs().max().item() <= 1e-2
+
+
+def test_split_domain_and_errors(dev):
+    G = n_cu(dev)
+    # outside the split's domain the query is 0 and fa_fwd_ws is fa_fwd
+    assert fa.fa_fwd_workspace_bytes(1, 24, 4600, 128, fa.FA_BF16) == 0      # N % 64 != 0
+    assert fa.fa_fwd_workspace_bytes(1, 24, 4608, 40, fa.FA_F16) == 0        # D != 128
+    assert fa.fa_fwd_workspace_bytes(1, 24, 4608, 128, fa.FA_F32) == 0      # fp32
+    assert fa.fa_fwd_workspace_bytes(1, 2, 4608, 128, fa.FA_BF16) == 0      # fewer blocks than CUs
+    assert fa.fa_fwd_workspace_bytes(1, 1, 256 * G, 128, fa.FA_BF16) == 0   # exactly one round
+    need = fa.fa_fwd_workspace_bytes(1, 24, 4608, 128, fa.FA_BF16)
+    assert need > 0
+    w = WORKLOADS[2].with_shape(H=2, N=1000)                                  # no split: plain fa_fwd
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    assert call_ws(q, k, v, o, None, None, w.scale) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), fa.fwd(q, k, v, split=False).view(torch.int16))
+    # the split shape without or with a short workspace is refused before any launch
+    q = torch.zeros((1, 24, 4608, 128), dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    assert call_ws(q, q, q, o, None, None, 0.1) == fa.FA_ERR_WORKSPACE
+    short = torch.zeros(need - 256, dtype=torch.uint8, device=dev)
+    assert call_ws(q, q, q, o, None, short, 0.1) == fa.FA_ERR_WORKSPACE
+    big = torch.zeros(need + 512, dtype=torch.uint8, device=dev)
+    assert fa.fa_fwd_ws(q.data_ptr(), q.data_ptr(), q.data_ptr(), o.data_ptr(), None, None, 1, 24, 4608, 128,
+                        0.1, fa.FA_BF16, big.data_ptr() + 16, need, None) == fa.FA_ERR_ALIGN
+
+
+def test_split_graph_replay(dev):
+    B, H, N = 1, 18, 4096
+    w = WORKLOADS[2].with_shape(B=B, H=H, N=N)
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    eager = fa.fwd(q, k, v).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fa.fwd(q, k, v, out=o)                 # warm-up: creates the stream's workspace
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            fa.fwd(q, k, v, out=o)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    for i in range(4):
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), eager.view(torch.int16)), f"replay {i}"

@@ -187,3 +187,22 @@ def test_int8qk_pv16_validation(lib):
     assert call(N=1 << 24) == fa.FA_ERR_SHAPE
     add = fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P, 0, 0, 0, 1)
     assert call(mask=ctypes.byref(add)) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fwd_ws_outside_split_domain(lib):
+    """Shapes the key-tile split does not take (decided before any device
+    query): the workspace size is 0 and fa_fwd_ws validates like fa_fwd."""
+    for B, H, N, D, dt in [(1, 24, 4608, 40, fa.FA_F16), (1, 24, 4608, 128, fa.FA_F32),
+                           (1, 24, 4600, 128, fa.FA_BF16), (0, 24, 4608, 128, fa.FA_BF16)]:
+        assert fa.fa_fwd_workspace_bytes(B, H, N, D, dt) == 0
+
+    def call(**kw):
+        a = dict(q=P, B=1, H=2, N=100, D=40, dtype=fa.FA_F16, scale=0.1, mask=None)
+        a.update(kw)
+        return fa.fa_fwd_ws(a["q"], P, P, P, None, a["mask"], a["B"], a["H"], a["N"], a["D"], a["scale"],
+                            a["dtype"], None, 0, None)
+    assert call(q=None) == fa.FA_ERR_NULL
+    assert call(D=64) == fa.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == fa.FA_ERR_ARG
+    assert call(B=0) == fa.FA_ERR_SHAPE
+    assert call(q=P + 8) == fa.FA_ERR_ALIGN

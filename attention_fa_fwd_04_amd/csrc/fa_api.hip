@@ -88,9 +88,37 @@ struct Layouts {
   fa::RowLayout q, k, v, o;
 };
 
+// Short query sequences (16-bit, Nq <= 64: batched window attention, whose
+// windows of 8x8 latents are 64 tokens, case-study page, section 3.2): one or
+// two waves per workgroup (32 or 64 query rows) so no wave idles on rows past
+// Nq; several workgroups share a CU.
+template <typename T, int D, int MASK, int NW>
+int launch_short(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
+                 const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
+  constexpr int BC = D >= 128 ? 32 : 64;       // D = 128: halves the tile staging registers
+  using C = fa::FwdCfg<T, D, BC, MASK, NW>;
+  const int nqt = (Nq + C::BR - 1) / C::BR;
+  const int64_t grid = (int64_t)B * H * nqt;
+  if (grid > INT32_MAX) return FA_ERR_SHAPE;
+  if (log_enabled())
+    std::fprintf(stderr, "[fa] fa_fwd(short) D=%d mask=%d B=%d H=%d Nq=%d Nk=%d grid=%lld block=%d BR=%d BC=%d lds=%d\n",
+                 D, MASK, B, H, Nq, Nk, (long long)grid, C::NT, C::BR, BC, 2 * C::BUF);
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, BC, MASK, NW, 2>), dim3((unsigned)grid), dim3(C::NT), 0, st,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                     static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e);
+  return record_launch("fa_fwd_kernel(short)");
+}
+constexpr int kShortRows = 64;
+
 template <typename T, int D, int MASK>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
                const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    // (D = 128 keeps two waves: one wave of it would hold a SIMD alone)
+    if constexpr (D < 128)
+      if (Nq <= 32) return launch_short<T, D, MASK, 1>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+    if (Nq <= kShortRows) return launch_short<T, D, MASK, 2>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+  }
   if constexpr (D == 128 && sizeof(T) == 2 && MASK != fa::kMaskAdd) {
     // 16-bit, D = 128, no score mask: the two wave groups of each SIMD
     // alternate between the MFMA and softmax phases, 8 waves x 64-key tiles

@@ -86,6 +86,9 @@ WORKLOADS = {
     # the Wan 2.1 inputs of workload 5 through the INT8-QK / 16-bit-PV form
     8: Workload(5, "wan-720p-int8qk-pv16", "bf16", 1, 40, 76112, 128,
                 k_offset_var=2.0, quantised=True, pv16=True, sampled_rows=512),
+    # window attention of an SD1.5 768^2 UNet block: the 96x96 latent cut into
+    # 8x8 windows (144 per image, 4 images) batched as 576 sequences of 64
+    9: Workload(9, "sd15-768-window8x8", "f16", 576, 8, 64, 40),
 }
 
 

@@ -1,6 +1,6 @@
 """Attention-forward throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2..9] [--no-cpu-baseline]
                     [--extra]
 
 One step is one pass of the hot path over one batch: a single fa_fwd call
@@ -225,7 +225,7 @@ def main() -> int:
         if split:
             u_ms, _ = measure(w, 20, 3, split=False)
             extra[w.name + " (fa_fwd, no split)"] = {"ms": round(u_ms, 4), "tflops": round(flops / (u_ms * 1e-3) / 1e12, 2)}
-        for wid in (3, 4, 5, 6, 7):
+        for wid in (3, 4, 5, 6, 7, 9):
             wx = WORKLOADS[wid]
             if wx.merge:
                 e_ms, _ = measure(wx, 50, 3)
@@ -235,7 +235,9 @@ def main() -> int:
             fl = 4.0 * wx.B * wx.H * wx.N * wx.n_keys * wx.D
             try:
                 e_ms, _ = measure(wx, 3 if wid in (4, 5) else 10, 1)
-                extra[wx.name] = {"ms": round(e_ms, 3), "tflops": round(fl / (e_ms * 1e-3) / 1e12, 2)}
+                io = 2.0 * wx.B * wx.H * (wx.N + wx.n_keys) * wx.D * (4 if wx.dtype == "f32" else 2)
+                extra[wx.name] = {"ms": round(e_ms, 3), "tflops": round(fl / (e_ms * 1e-3) / 1e12, 2),
+                                  "GB/s": round(io / (e_ms * 1e-3) / 1e9, 1)}
             except fa.FAError as e:
                 extra[wx.name] = {"error": str(e)}
             if wx.quantised:

@@ -53,10 +53,12 @@
 // block-major order, so a workgroup finishes the key tiles of a block its
 // predecessor started, takes whole blocks, and starts a block its successor
 // finishes.  A block split between two workgroups is the same online
-// softmax over two disjoint key ranges: each part leaves its unnormalised
-// accumulator, running max and denominator in the workspace, and the part
-// that arrives second (an arrival counter per split) combines the two by
-// the handbook's rescale, exp(m_part - m), and stores O and lse.  The
+// softmax over two disjoint key ranges: the part that arrives first (an
+// arrival counter per split) leaves its unnormalised accumulator, running
+// max and denominator in the workspace, and the part that arrives second
+// combines the two by the handbook's rescale, exp(m_part - m), and stores O
+// and lse.  A part writes its partial unless it finds the other counted
+// already; both write only if they arrive together.  The
 // combination is written as a function of (first-range part, second-range
 // part) whichever arrives last, so the result does not depend on arrival
 // order.  Both split parts of a workgroup run before its whole blocks, so
@@ -475,17 +477,23 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
       const uint32_t other = (uint32_t)(slot * 2 + (1 - part)) * (uint32_t)kPartFloats * 4u;
       const uint32_t lane_acc = (uint32_t)(wave * 16 * 64 + lane) * 16u;
       const uint32_t lane_ml = (uint32_t)kPartAccFloats * 4u + (uint32_t)(wave * 64 + lane) * 8u;
+      // A part that finds the other already counted skips writing its own:
+      // the counter reaches 1 only after that part's partial is written.
+      if (tid == 0) arrival = __hip_atomic_load(sk.cnt + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (arrival == 0) {
 #pragma unroll
-      for (int p = 0; p < PVB; ++p)
+        for (int p = 0; p < PVB; ++p)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 x = {acc[p][4 * g], acc[p][4 * g + 1], acc[p][4 * g + 2], acc[p][4 * g + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), pr,
-                                                 (int)(mine + lane_acc + (4 * p + g) * 64 * 16), 0, kDeviceScope);
-        }
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{m_run, l_tot}), pr,
-                                            (int)(mine + lane_ml), 0, kDeviceScope);
-      __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's part is written
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 x = {acc[p][4 * g], acc[p][4 * g + 1], acc[p][4 * g + 2], acc[p][4 * g + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), pr,
+                                                   (int)(mine + lane_acc + (4 * p + g) * 64 * 16), 0, kDeviceScope);
+          }
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{m_run, l_tot}), pr,
+                                              (int)(mine + lane_ml), 0, kDeviceScope);
+        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wave's part is written
+      }
       __syncthreads();
       if (tid == 0) arrival = atomicInc(sk.cnt + slot, 1u);
       __syncthreads();

@@ -81,11 +81,23 @@ def cpu_baseline(w, budget_s: float = 20.0, min_s: float = 10.0) -> dict:
             break
     flops = 4.0 * done * w.N * w.n_keys * w.D
     cores = len(os.sched_getaffinity(0))
+    cpu, blas = "unknown CPU", "unknown BLAS"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()
+                                 if p.get("user_api") == "blas"})) or blas
+    except Exception:
+        pass
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores,
             "kind": "oracle",
             "sample": f"{done} head evaluations ({passes} pass(es) over the {len(heads)} heads) of {w.name} "
                       f"(N={w.N}, Nk={w.n_keys}, D={w.D}), numpy float64 naive formula, {t_total:.1f} s, "
-                      f"BLAS threads {blas_threads}, host cores {cores}"}
+                      f"BLAS {blas} with {blas_threads} threads, host cores {cores}, {cpu}"}
 
 
 def main() -> int:

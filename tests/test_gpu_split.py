@@ -207,3 +207,25 @@ def test_split_graph_replay(dev):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+
+
+def test_split_two_streams(dev):
+    """fwd() keeps one workspace per (device, stream): the same layer queued on
+    two streams at once gives the same output on both."""
+    w = WORKLOADS[2].with_shape(H=18, N=4096)
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    ref = fa.fwd(q, k, v, split=False)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    outs = []
+    for s in (s1, s2):
+        with torch.cuda.stream(s):
+            outs.append(torch.empty_like(q))
+    for _ in range(3):
+        for s, o in zip((s1, s2), outs):
+            with torch.cuda.stream(s):
+                fa.fwd(q, k, v, out=o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert (outs[0].float() - ref.float()).abs().max().item() <= 1e-2

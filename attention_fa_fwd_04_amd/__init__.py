@@ -26,7 +26,7 @@ FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
 EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_fwd_cross", "fa_fwd_strided",
             "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk",
             "fa_fwd_int8qk_pv16_workspace_bytes", "fa_fwd_int8qk_pv16",
-            "fa_merge", "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
+            "fa_merge", "fa_mfma_probe", "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
 
 class FAUnavailable(RuntimeError):
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     h.fa_fwd_int8qk_pv16.restype = i32
     h.fa_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     h.fa_merge.restype = i32
+    h.fa_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
+    h.fa_mfma_probe.restype = i32
     h.fa_int8qk_kv_block.argtypes = []
     h.fa_int8qk_kv_block.restype = i32
     h.fa_status_string.argtypes = [i32]
@@ -149,6 +151,45 @@ def fa_fwd_int8qk_pv16(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspac
 
 def fa_merge(o_a, lse_a, o_b, lse_b, o, lse, B, H, N, D, dtype, hip_stream) -> int:
     return lib().fa_merge(o_a, lse_a, o_b, lse_b, o, lse, B, H, N, D, dtype, hip_stream)
+
+
+def fa_mfma_probe(kind, workgroups, iters, out, hip_stream) -> int:
+    return lib().fa_mfma_probe(kind, workgroups, iters, out, hip_stream)
+
+
+PROBE_FLOPS = {0: 2.0 * 32 * 32 * 16, 1: 2.0 * 32 * 32 * 64, 2: 2.0 * 32 * 32 * 32}
+
+
+def mfma_peak(kind: int, ms_target: float = 40.0, device=None, warmup_ms: float = 150.0) -> float:
+    """Sustained dense MFMA rate (TFLOP/s or TOP/s) of one shape on the
+    current GPU from fa_mfma_probe: kind 0 bf16, 1 fp8 e4m3, 2 int8.  After
+    about warmup_ms of the probe (the clock ramps up from idle), the median
+    of three runs of about ms_target milliseconds: the rate the part holds
+    under load."""
+    import torch
+    dev = device or torch.device("cuda", torch.cuda.current_device())
+    wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(4 * wgs, dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream(dev)
+
+    def run(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        rc = fa_mfma_probe(kind, wgs, iters, out.data_ptr(), st.cuda_stream)
+        e1.record(st)
+        if rc != FA_OK:
+            raise FAError(rc, "fa_mfma_probe")
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1)
+
+    iters = 2000
+    t = run(iters)
+    iters = max(iters, int(iters * ms_target / max(t, 1e-3)))
+    spent = 0.0
+    while spent < warmup_ms:
+        spent += run(iters)
+    ts = sorted(run(iters) for _ in range(3))
+    return wgs * 16 * iters * PROBE_FLOPS[kind] / (ts[1] * 1e-3) / 1e12
 
 
 def fa_int8qk_kv_block() -> int:

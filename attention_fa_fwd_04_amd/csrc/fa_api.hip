@@ -14,6 +14,7 @@
 #include "fa_fwd_pp.hpp"
 #include "fa_int8qk.hpp"
 #include "fa_merge.hpp"
+#include "fa_probe.hpp"
 
 // Tile configuration of fa_fwd_kernel (fp32, and 16-bit D = 32 / 40; 16-bit
 // D = 128 runs fa_fwd_pp_kernel or fa_fwd_dma_kernel): D = 128 (fp32) runs
@@ -469,6 +470,27 @@ FA_API int fa_merge(const void* o_a, const float* lse_a, const void* o_b, const 
       break;
   }
   return record_launch("fa_merge_kernel");
+}
+
+FA_API int fa_mfma_probe(int kind, int workgroups, int iters, float* out, void* hip_stream) {
+  if (!out) return FA_ERR_NULL;
+  if (workgroups <= 0 || iters <= 0) return FA_ERR_SHAPE;
+  if (!aligned(out, 4)) return FA_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  switch (kind) {
+    case fa::kProbeBf16:
+      hipLaunchKernelGGL((fa::fa_mfma_probe_kernel<fa::kProbeBf16>), dim3(workgroups), dim3(256), 0, st, out, iters);
+      break;
+    case fa::kProbeFp8:
+      hipLaunchKernelGGL((fa::fa_mfma_probe_kernel<fa::kProbeFp8>), dim3(workgroups), dim3(256), 0, st, out, iters);
+      break;
+    case fa::kProbeInt8:
+      hipLaunchKernelGGL((fa::fa_mfma_probe_kernel<fa::kProbeInt8>), dim3(workgroups), dim3(256), 0, st, out, iters);
+      break;
+    default:
+      return FA_ERR_ARG;
+  }
+  return record_launch("fa_mfma_probe_kernel");
 }
 
 FA_API int fa_int8qk_kv_block(void) { return fa::kInt8Bc; }

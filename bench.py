@@ -107,6 +107,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the MFMA-only peak probe")
     ap.add_argument("--extra", action="store_true", help="also time the other full-size workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (scales HBM byte counters)")
@@ -222,6 +223,15 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(tflops_kernel / peak, 4),
                      "traffic": traffic_for(kernel_key)},
     }
+    # The sustained MFMA rate of the kernel's data type from an MFMA-only
+    # probe: the fraction of what the part holds under load, next to the
+    # fraction of the published peak.
+    if not args.no_probe and w.dtype != "f32":
+        kinds = {"int8": 2, "fp8": 1} if w.quantised else {"bf16" if w.dtype == "bf16" else "f16": 0}
+        mp = {name: round(fa.mfma_peak(kind, device=dev), 1) for name, kind in kinds.items()}
+        out["roofline"]["measured_peak"] = mp
+        if not w.quantised:
+            out["roofline"]["frac_of_measured_peak"] = round(tflops_kernel / next(iter(mp.values())), 4)
     # Q and O once, K and V once: with few keys (cross-attention on a short
     # text sequence) moving these bytes takes longer than the MFMA work
     elt = 4 if w.dtype == "f32" else 2

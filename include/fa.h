@@ -238,6 +238,22 @@ FA_API int fa_merge(const void* o_a, const float* lse_a, const void* o_b, const 
                     void* o, float* lse, int B, int H, int N, int D, fa_dtype_t dtype,
                     void* hip_stream);
 
+/*
+ * Measurement aid, not part of the attention path: an MFMA-only throughput
+ * probe giving the dense matrix-core rate the part sustains (the published
+ * peaks assume the 2.4 GHz peak engine clock).  Launches `workgroups`
+ * workgroups of 4 waves; every wave issues 4 x iters independent MFMAs of
+ * one shape on hashed, finite operands and writes one float to
+ * out[4 * workgroup + wave] (out: 4 * workgroups floats, device memory).
+ *   kind 0: v_mfma_f32_32x32x16_bf16   (32768 flop each)
+ *   kind 1: v_mfma_f32_32x32x64_f8f6f4 (e4m3, 131072 flop each)
+ *   kind 2: v_mfma_i32_32x32x32_i8     (65536 op each)
+ * Total work = workgroups * 16 * iters * (flop each); time it with events on
+ * hip_stream.  Errors: FA_ERR_NULL, FA_ERR_SHAPE (workgroups or iters <= 0),
+ * FA_ERR_ALIGN, FA_ERR_ARG (kind).
+ */
+FA_API int fa_mfma_probe(int kind, int workgroups, int iters, float* out, void* hip_stream);
+
 /* Keys per tile of the quantised variant's online softmax (P is rounded
  * against the running max, so the result depends on this tile size). */
 FA_API int fa_int8qk_kv_block(void);

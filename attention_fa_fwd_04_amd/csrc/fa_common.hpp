@@ -136,5 +136,17 @@ __device__ __forceinline__ float wave_max_halves(float x) {
 __device__ __forceinline__ float wave_sum_halves(float x) {
   return x + __shfl_xor(x, 32);
 }
+// The same max through v_permlane32_swap: swap(v, v) leaves {own, other
+// half's} value in its two results on every lane (in either order), a VALU
+// exchange with no trip through the LDS crossbar, and max is symmetric in
+// the pair, so both halves get the same result.  Used where the exchange
+// is on every tile's critical path (the quantised kernel's exact row max);
+// the D = 128 16-bit kernels keep the crossbar form, which the register
+// allocator handles better in their tile loops.
+__device__ __forceinline__ float wave_max_halves_valu(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
 
 }  // namespace fa

@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
         }
       mx = (float)imx * c;
     }
-    mx = wave_max_halves(mx);
+    mx = wave_max_halves_valu(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
         }
       mx = (float)imx * c;
     }
-    mx = wave_max_halves(mx);
+    mx = wave_max_halves_valu(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);

@@ -273,6 +273,7 @@ SplitPlan split_plan(int B, int H, int N, int D, int dtype, int mask_kind) {
   SplitPlan p;
   if ((dtype != FA_F16 && dtype != FA_BF16) || D != 128 || mask_kind != FA_MASK_NONE) return p;
   if (B <= 0 || H <= 0 || N <= 0 || N % kSplitBC != 0) return p;
+  if (N <= kShortRows) return p;               // short sequences: one- or two-wave workgroups
   const int G = cu_count();
   if (G <= 0) return p;
   const int nqt = (N + kSplitBR - 1) / kSplitBR;

@@ -89,10 +89,11 @@ struct Layouts {
   fa::RowLayout q, k, v, o;
 };
 
-// Short query sequences (16-bit, Nq <= 64: batched window attention, whose
-// windows of 8x8 latents are 64 tokens, case-study page, section 3.2): one or
-// two waves per workgroup (32 or 64 query rows) so no wave idles on rows past
-// Nq; several workgroups share a CU.
+// Short query sequences (16-bit, Nq <= 128: batched window attention, whose
+// windows of 8x8 latents are 64 tokens, case-study page, section 3.2): one,
+// two or four waves per workgroup (32, 64 or 128 query rows) so no wave idles
+// on rows past Nq (the D = 128 kernels take 256 rows); several workgroups
+// share a CU.
 template <typename T, int D, int MASK, int NW>
 int launch_short(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
                  const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
@@ -109,7 +110,7 @@ int launch_short(const void* q, const void* k, const void* v, void* o, float* ls
                      static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e);
   return record_launch("fa_fwd_kernel(short)");
 }
-constexpr int kShortRows = 64;
+constexpr int kShortRows = 128;
 
 template <typename T, int D, int MASK>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
@@ -118,7 +119,8 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     // (D = 128 keeps two waves: one wave of it would hold a SIMD alone)
     if constexpr (D < 128)
       if (Nq <= 32) return launch_short<T, D, MASK, 1>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
-    if (Nq <= kShortRows) return launch_short<T, D, MASK, 2>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+    if (Nq <= 64) return launch_short<T, D, MASK, 2>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+    if (Nq <= kShortRows) return launch_short<T, D, MASK, 4>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
   }
   if constexpr (D == 128 && sizeof(T) == 2 && MASK != fa::kMaskAdd) {
     // 16-bit, D = 128, no score mask: the two wave groups of each SIMD
@@ -273,7 +275,7 @@ SplitPlan split_plan(int B, int H, int N, int D, int dtype, int mask_kind) {
   SplitPlan p;
   if ((dtype != FA_F16 && dtype != FA_BF16) || D != 128 || mask_kind != FA_MASK_NONE) return p;
   if (B <= 0 || H <= 0 || N <= 0 || N % kSplitBC != 0) return p;
-  if (N <= kShortRows) return p;               // short sequences: one- or two-wave workgroups
+  if (N <= kShortRows) return p;               // short sequences: the one/two/four-wave workgroups
   const int G = cu_count();
   if (G <= 0) return p;
   const int nqt = (N + kSplitBR - 1) / kSplitBR;

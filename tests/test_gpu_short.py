@@ -1,8 +1,8 @@
-"""Short query sequences (Nq <= 64): batched window attention.
+"""Short query sequences (Nq <= 128): batched window attention.
 
 The case-study page (section 3.2) cuts the latent into non-overlapping 8x8
 windows and runs attention inside each, batched over windows; such calls
-take workgroups of one or two waves (32 or 64 query rows).  Parity with the
+take workgroups of one, two or four waves (32, 64 or 128 query rows).  Parity with the
 CPU oracle element by element, for every head dimension, 16-bit dtype and
 mask kind, window sizes on both sides of 32 rows, cross-attention with a
 short query side, strided views, and the full SD1.5 window workload.
@@ -58,7 +58,7 @@ def oracle(inp, scale, mask=None, key_len=None):
 @pytest.mark.parametrize("D", [32, 40, 128])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_windows(dev, dt, D, mask_kind):
-    for B, H, N in [(40, 2, 16), (24, 3, 32), (12, 4, 49), (20, 3, 64)]:
+    for B, H, N in [(40, 2, 16), (24, 3, 32), (12, 4, 49), (20, 3, 64), (6, 3, 100), (5, 2, 128)]:
         w = Workload(120 + D, f"window-{dt}", dt, B, H, N, D)
         inp = make_inputs(w)
         kl = mask = None
@@ -82,7 +82,7 @@ def test_windows(dev, dt, D, mask_kind):
 @pytest.mark.parametrize("D", [40, 128])
 def test_short_queries_long_keys(dev, D):
     """Cross-attention with a short query side: Nq <= 64 rows, many key tiles."""
-    for Nq, Nk in [(1, 77), (30, 300), (64, 1000)]:
+    for Nq, Nk in [(1, 77), (30, 300), (64, 1000), (120, 700)]:
         w = Workload(130 + D, "short-cross", "f16", 3, 2, Nq, D, Nk=Nk)
         inp = make_inputs(w)
         say(f"case short-cross D={D} Nq={Nq} Nk={Nk}")

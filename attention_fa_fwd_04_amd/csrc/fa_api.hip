@@ -89,11 +89,12 @@ struct Layouts {
   fa::RowLayout q, k, v, o;
 };
 
-// Short query sequences (16-bit, Nq <= 128: batched window attention, whose
+// Short query sequences (16-bit, Nq <= 384: batched window attention, whose
 // windows of 8x8 latents are 64 tokens, case-study page, section 3.2): one,
 // two or four waves per workgroup (32, 64 or 128 query rows) so no wave idles
-// on rows past Nq (the D = 128 kernels take 256 rows); several workgroups
-// share a CU.
+// on rows past Nq; several workgroups share a CU.  For D = 128 the four-wave
+// form beats the 256-row phase-alternating kernel up to 384 query rows
+// (measured; from 512 the latter is faster).
 template <typename T, int D, int MASK, int NW>
 int launch_short(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
                  const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
@@ -110,7 +111,7 @@ int launch_short(const void* q, const void* k, const void* v, void* o, float* ls
                      static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e);
   return record_launch("fa_fwd_kernel(short)");
 }
-constexpr int kShortRows = 128;
+constexpr int kShortRows = 384;
 
 template <typename T, int D, int MASK>
 int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,

@@ -146,7 +146,7 @@ FA_API int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, 
  *     CURRENT device (it depends on the CU count), or 0 when the shape does
  *     not take the split: then fa_fwd_ws is fa_fwd and ignores workspace.
  *     The split is taken for dtype F16/BF16, D = 128, no mask (NULL or
- *     FA_MASK_NONE), N a multiple of 64 and above 128, at least one query
+ *     FA_MASK_NONE), N a multiple of 64 and above 384, at least one query
  *     block per CU.
  *   workspace: 256-byte aligned device memory of at least that size, all
  *     zero before its first use.  It begins with one arrival counter per

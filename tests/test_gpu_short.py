@@ -1,4 +1,4 @@
-"""Short query sequences (Nq <= 128): batched window attention.
+"""Short query sequences (Nq <= 384): batched window attention.
 
 The case-study page (section 3.2) cuts the latent into non-overlapping 8x8
 windows and runs attention inside each, batched over windows; such calls
@@ -58,7 +58,7 @@ def oracle(inp, scale, mask=None, key_len=None):
 @pytest.mark.parametrize("D", [32, 40, 128])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_windows(dev, dt, D, mask_kind):
-    for B, H, N in [(40, 2, 16), (24, 3, 32), (12, 4, 49), (20, 3, 64), (6, 3, 100), (5, 2, 128)]:
+    for B, H, N in [(40, 2, 16), (24, 3, 32), (12, 4, 49), (20, 3, 64), (6, 3, 100), (5, 2, 128), (3, 2, 300)]:
         w = Workload(120 + D, f"window-{dt}", dt, B, H, N, D)
         inp = make_inputs(w)
         kl = mask = None

@@ -45,7 +45,7 @@ def takes_split(dev, B, H, N):
     G = n_cu(dev)
     J = blocks(B, H, N)
     rounds = (J + G - 1) // G
-    return N % 64 == 0 and N > 128 and J >= G and J * 10 < rounds * G * 9
+    return N % 64 == 0 and N > 384 and J >= G and J * 10 < rounds * G * 9
 
 
 def call_ws(q, k, v, o, lse, ws, scale, dt=fa.FA_BF16):
@@ -166,6 +166,7 @@ def test_split_domain_and_errors(dev):
     assert fa.fa_fwd_workspace_bytes(1, 1, 256 * G, 128, fa.FA_BF16) == 0   # exactly one round
     assert fa.fa_fwd_workspace_bytes(1, 300, 64, 128, fa.FA_BF16) == 0       # short sequences
     assert fa.fa_fwd_workspace_bytes(1, 300, 128, 128, fa.FA_BF16) == 0
+    assert fa.fa_fwd_workspace_bytes(1, 300, 384, 128, fa.FA_BF16) == 0
     need = fa.fa_fwd_workspace_bytes(1, 24, 4608, 128, fa.FA_BF16)
     assert need > 0
     w = WORKLOADS[2].with_shape(H=2, N=1000)                                  # no split: plain fa_fwd

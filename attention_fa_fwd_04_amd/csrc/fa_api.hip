@@ -95,21 +95,33 @@ struct Layouts {
 // on rows past Nq; several workgroups share a CU.  For D = 128 the four-wave
 // form beats the 256-row phase-alternating kernel up to 384 query rows
 // (measured; from 512 the latter is faster).
-template <typename T, int D, int MASK, int NW>
-int launch_short(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
-                 const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
-  constexpr int BC = D >= 128 ? 32 : 64;       // D = 128: halves the tile staging registers
+template <typename T, int D, int MASK, int NW, int BC, bool ONE_TILE>
+int launch_short_cfg(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
+                     const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
   using C = fa::FwdCfg<T, D, BC, MASK, NW>;
   const int nqt = (Nq + C::BR - 1) / C::BR;
   const int64_t grid = (int64_t)B * H * nqt;
   if (grid > INT32_MAX) return FA_ERR_SHAPE;
   if (log_enabled())
     std::fprintf(stderr, "[fa] fa_fwd(short) D=%d mask=%d B=%d H=%d Nq=%d Nk=%d grid=%lld block=%d BR=%d BC=%d lds=%d\n",
-                 D, MASK, B, H, Nq, Nk, (long long)grid, C::NT, C::BR, BC, 2 * C::BUF);
-  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, BC, MASK, NW, 2>), dim3((unsigned)grid), dim3(C::NT), 0, st,
+                 D, MASK, B, H, Nq, Nk, (long long)grid, C::NT, C::BR, BC, (ONE_TILE ? 1 : 2) * C::BUF);
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<T, D, BC, MASK, NW, 2, ONE_TILE>), dim3((unsigned)grid), dim3(C::NT), 0, st,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                      static_cast<T*>(o), lse, m, L.q, L.k, L.v, L.o, H, Nq, Nk, nqt, scale * fa::kLog2e);
   return record_launch("fa_fwd_kernel(short)");
+}
+
+template <typename T, int D, int MASK, int NW>
+int launch_short(const void* q, const void* k, const void* v, void* o, float* lse, fa::MaskArgs m,
+                 const Layouts& L, int B, int H, int Nq, int Nk, float scale, hipStream_t st) {
+  // D < 128 with all keys in one 64-key tile (windows): one LDS buffer and
+  // no prefetch registers, so more workgroups fit on a CU (576x8 windows of
+  // 64, D = 40: 25.0 -> 18.9 us; for D = 128 it measured slower).  Otherwise
+  // double-buffered tiles, of 32 keys for D = 128 (whose staging registers
+  // would leave one wave per SIMD with 64).
+  if constexpr (D < 128)
+    if (Nk <= 64) return launch_short_cfg<T, D, MASK, NW, 64, true>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
+  return launch_short_cfg<T, D, MASK, NW, (D >= 128 ? 32 : 64), false>(q, k, v, o, lse, m, L, B, H, Nq, Nk, scale, st);
 }
 constexpr int kShortRows = 384;
 

@@ -65,14 +65,18 @@ struct FwdCfg {
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
-template <typename T, int D, int BC, int MASK, int NW, int MINB>
+// ONE_TILE: every key fits in one tile (Nk <= BC, guaranteed by the caller):
+// one LDS buffer and no prefetch, so more workgroups fit on a CU (batched
+// short windows).
+template <typename T, int D, int BC, int MASK, int NW, int MINB, bool ONE_TILE = false>
 __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, MaskArgs mask,
     RowLayout lq, RowLayout lk, RowLayout lv, RowLayout lo,
     int H, int Nq, int Nk, int nqt, float c_log2) {
   using C = FwdCfg<T, D, BC, MASK, NW>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::BUF];
+  constexpr int NBUF = ONE_TILE ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
   // Zero the padding the tile writes never touch: K chunks past D (QK steps
   // are 2 chunks wide) and V^T rows past D (PV blocks are 32 channels).
   if constexpr (2 * C::QKS > C::DCH) {
-    for (int r = tid; r < 2 * BC; r += C::NT) {
+    for (int r = tid; r < NBUF * BC; r += C::NT) {
       uint8_t* p = smem + (r / BC) * C::BUF + (r % BC) * C::KSTR + C::DCH * 16;
       for (int c = 0; c < (2 * C::QKS - C::DCH) * 16; c += 16)
         *reinterpret_cast<u32x4*>(p + c) = u32x4{0u, 0u, 0u, 0u};
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
   if constexpr (32 * C::PVB > D) {
     constexpr int rows = 32 * C::PVB - D;
     constexpr int chunks = BC * C::E / 16;
-    for (int it = tid; it < 2 * rows * chunks; it += C::NT) {
+    for (int it = tid; it < NBUF * rows * chunks; it += C::NT) {
       const int buf = it / (rows * chunks), rem = it % (rows * chunks);
       uint8_t* p = smem + buf * C::BUF + C::KBYTES + (D + rem / chunks) * C::VSTR + (rem % chunks) * 16;
       *reinterpret_cast<u32x4*>(p) = u32x4{0u, 0u, 0u, 0u};
@@ -219,8 +223,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
   // unless the mask is additive.
   auto step = [&](int j, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const int buf = j & 1;
-    load_tile(j + 1);
+    const int buf = ONE_TILE ? 0 : (j & 1);
+    if constexpr (!ONE_TILE) load_tile(j + 1);
     const uint8_t* kb = smem + buf * C::BUF;
     const uint8_t* vb = kb + C::KBYTES;
     const int kv0 = j * BC;
@@ -315,8 +319,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
       }
     }
 
-    store_tile(buf ^ 1);
-    __syncthreads();
+    if constexpr (!ONE_TILE) {
+      store_tile(buf ^ 1);
+      __syncthreads();
+    }
   };
 
   load_tile(0);

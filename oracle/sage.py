@@ -19,7 +19,10 @@ way on both sides:
   * FP8 V: one scale per (b, h, channel): av = max_t |V|,
     v8 = e4m3(fp32(V * fp32(448 / av))), sv = fp32(av / 448).
   * Scores s = (sum_d q8 k8) * sq * sk * scale (the integer dot product is
-    exact), then the mask as in the unquantised formula.
+    exact), then the mask as in the unquantised formula: an additive mask is
+    added to the dequantised, scaled scores (scale first, then the mask, as
+    the case-study page's attention code does in its section 2.3), before
+    the running max; a key-length mask drops the keys at and past the length.
   * P is quantised against the running max of the blocked recurrence: for the
     key tiles of ``kv_block`` keys in ascending order, m_j = max(m_{j-1},
     tile max), P = exp(s - m_j) <= 1, l = l * exp(m_{j-1} - m_j) + sum P (the
@@ -95,11 +98,12 @@ def quantise_head(q_head, k_head, v_head):
 
 
 def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quantise_p=True,
-                              return_lse=False, pv="fp8"):
+                              return_lse=False, pv="fp8", mask=None):
     """Blocked recurrence over key tiles with P quantised against the running max.
     The lse is that of the quantised, smoothed scores (natural log).  pv selects
     the P V arithmetic: "fp8" (448 P and V in e4m3) or "bf16" / "f16" (P rounded
-    to that type, V unquantised)."""
+    to that type, V unquantised).  mask: additive values [len(row_ids), N] for
+    the selected rows (-inf drops a key), added after scaling."""
     if pv == "fp8":
         vmat, pmul, pround = qz["v8"], E4M3_MAX, round_e4m3
     elif pv in ("bf16", "f16"):
@@ -114,6 +118,8 @@ def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quanti
     s = s * qz["sq"][row_ids // QBLOCK].astype(np.float64)[:, None]
     s = s * qz["sk"][np.arange(n) // QBLOCK].astype(np.float64)[None, :]
     s = s * float(scale)
+    if mask is not None:
+        s = s + np.broadcast_to(np.asarray(mask, dtype=np.float64), s.shape)
     if key_len is not None:
         s[:, int(key_len):] = -np.inf
     R = len(row_ids)
@@ -142,24 +148,29 @@ def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quanti
 
 
 def emulate_rows(q_head, k_head, v_head, row_ids, scale, kv_block, key_len=None, qz=None,
-                 return_lse=False, pv="fp8"):
+                 return_lse=False, pv="fp8", mask=None):
     """Quantised-variant output for selected query rows of one head (float64, before
     the output rounding); with return_lse also the rows' log-sum-exp of the
-    smoothed quantised scores."""
+    smoothed quantised scores.  mask: additive values for the selected rows,
+    broadcastable to [len(row_ids), N]."""
     if qz is None:
         qz = quantise_head(q_head, k_head, v_head)
-    return _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len, return_lse=return_lse, pv=pv)
+    return _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len, return_lse=return_lse, pv=pv,
+                                     mask=mask)
 
 
-def emulate(q, k, v, scale, kv_block, key_len=None, return_lse=False, pv="fp8"):
-    """Full [B, H, N, D] emulation (small shapes)."""
+def emulate(q, k, v, scale, kv_block, key_len=None, return_lse=False, pv="fp8", mask=None):
+    """Full [B, H, N, D] emulation (small shapes); mask broadcastable to
+    [B, H, N, N] (additive)."""
     q = np.asarray(q)
     B, H, N, D = q.shape
     out = np.zeros((B, H, N, np.asarray(v).shape[3]))
     lse = np.zeros((B, H, N))
+    mfull = None if mask is None else np.broadcast_to(np.asarray(mask, dtype=np.float64), (B, H, N, N))
     for b in range(B):
         for h in range(H):
             kl = None if key_len is None else int(np.asarray(key_len)[b])
             out[b, h], lse[b, h] = emulate_rows(q[b, h], k[b, h], v[b, h], np.arange(N), scale, kv_block,
-                                                kl, return_lse=True, pv=pv)
+                                                kl, return_lse=True, pv=pv,
+                                                mask=None if mfull is None else mfull[b, h])
     return (out, lse) if return_lse else out

@@ -207,3 +207,101 @@ def test_cosine_against_unquantised_on_wan_recipe(kv_block):
         assert np.abs(o - ref).max() < 5e-2          # loose: the bound that binds is the cosine
     print("cosines", cos)
     assert min(cos) >= 0.99
+
+
+# ---- P rounding against the running max (reading R14), hand-derived values ----
+
+def _three_key_row():
+    """One query, three keys, D = 1, every scale 1: integer scores 0, -1, +1
+    times c = -ln 0.3, so exp(s) = 1, 0.3 and 1 / 0.3.  V codes 1, 2, 0 with
+    a channel scale of 1."""
+    qz = dict(q8=np.array([[1]], dtype=np.int8), sq=np.float32([1.0]),
+              k8=np.array([[0], [-1], [1]], dtype=np.int8), sk=np.float32([1.0]),
+              v8=np.array([[1.0], [2.0], [0.0]]), sv=np.float32([1.0]))
+    return qz, -math.log(0.3)
+
+
+def test_p_rounded_against_running_max_hand_derived():
+    """Key tiles of 2: tile 0 = keys 0, 1; tile 1 = key 2.
+
+    Tile 0 (running max 0): P = 1, 0.3; 448 P = 448 (an e4m3 value) and 134.4,
+    which rounds to 128 (e4m3 spacing 16 in [128, 256)); acc = 448*1 + 128*2
+    = 704, l = 1.3.  Tile 1 raises the max to c: both are rescaled by
+    exp(-c) = 0.3 (acc 211.2, l 0.39), key 2 adds P = 1 (448 * 0 to acc):
+    l = 1.39, O = 211.2 / (448 * 1.39).
+
+    Rounding against the final max instead would give 448*0.3 = 134.4 -> 128
+    and 448*0.09 = 40.32 -> 40 (spacing 4 in [32, 64)): O = 208 / (448 * 1.39),
+    which is what a single tile holding all three keys gives."""
+    qz, c = _three_key_row()
+    o, lse = sage._quantised_attention_rows(np.array([0]), qz, c, kv_block=2, return_lse=True)
+    running = 0.3 * (448.0 * 1 + 128.0 * 2) / (448.0 * 1.39)
+    final = (128.0 * 1 + 40.0 * 2) / (448.0 * 1.39)
+    assert abs(running - final) > 1e-3                      # the readings really differ here
+    assert abs(o[0, 0] - running) < 1e-12
+    o1 = sage._quantised_attention_rows(np.array([0]), qz, c, kv_block=3)
+    assert abs(o1[0, 0] - final) < 1e-12
+    # l sums the unrounded P: lse is the exact log-sum-exp of the three scores
+    assert abs(lse[0] - math.log(1 + 0.3 + 1 / 0.3)) < 1e-12
+
+
+def test_p_rounding_16bit_pv_hand_derived():
+    """The same scores with P V in bf16 and V = 1, 3, 0 (unquantised): tile 0
+    rounds P = 0.3 to bf16 (0.30078125, the nearest value with 8 significant
+    bits), then rescales by 0.3; against the final max P = 0.3 and 0.09 would
+    round to 0.30078125 and 0.08984375."""
+    qz, c = _three_key_row()
+    qz["v16"] = np.array([[1.0], [3.0], [0.0]])
+    o = sage._quantised_attention_rows(np.array([0]), qz, c, kv_block=2, pv="bf16")
+    running = 0.3 * (1.0 + 0.30078125 * 3) / 1.39
+    final = (0.30078125 + 0.08984375 * 3) / 1.39
+    assert abs(running - final) > 1e-4
+    assert abs(o[0, 0] - running) < 1e-12
+
+
+# ---- additive mask in the emulation ----
+
+@pytest.mark.parametrize("pv", ["fp8", "bf16"])
+def test_lossless_case_with_additive_mask_equals_unquantised_formula(pv):
+    """Mask values on the ln 2 grid ({-ln 2, 0, ln 2}) and -inf keep every P a
+    power of two within the exact e4m3 range, so the emulation must equal the
+    unquantised formula with the mask added after scaling.  Rows with every
+    key masked give O = 0 and lse = -inf."""
+    q, k, v, step_q, step_k = _lossless_head(5)
+    n = len(q)
+    scale = math.log(2) / (step_q * step_k)
+    rng = np.random.default_rng(31)
+    mask = rng.choice([-math.log(2), 0.0, math.log(2)], (n, n))
+    mask[rng.random((n, n)) < 0.3] = -np.inf
+    mask[7] = -np.inf                                        # a fully masked row
+    mask[:, 64:128] = np.where(np.arange(n)[:, None] % 3 == 0, -np.inf, mask[:, 64:128])   # dead tiles
+    o_emu, lse_emu = sage.emulate_rows(q, k, v, np.arange(n), scale, 64, pv=pv, mask=mask, return_lse=True)
+    o_ref, lse_ref = attention.naive(q[None, None], k[None, None], v[None, None], scale, mask=mask[None, None])
+    assert np.abs(o_emu - o_ref[0, 0]).max() <= 1e-12 * np.abs(v).max()
+    assert np.all(o_emu[7] == 0) and np.isneginf(lse_emu[7])
+    fin = np.isfinite(lse_ref[0, 0])
+    assert np.array_equal(fin, np.isfinite(lse_emu))
+    assert np.abs(lse_emu[fin] - lse_ref[0, 0][fin]).max() < 1e-9
+
+
+def test_constant_additive_mask_shifts_lse_only():
+    """A constant mask c moves every score and every running max by c: O is
+    unchanged and lse moves by c (softmax's shift invariance, with P taken
+    against the shifted running max)."""
+    from attention_fa_fwd_04_amd.workloads import WORKLOADS, head
+    w = WORKLOADS[5].with_shape(N=300)
+    q, k, v = (head(w, t, 0, 0).double().numpy() for t in range(3))
+    rows = np.arange(0, 300, 3)
+    o0, l0 = sage.emulate_rows(q, k, v, rows, w.scale, 64, return_lse=True)
+    o1, l1 = sage.emulate_rows(q, k, v, rows, w.scale, 64, return_lse=True, mask=-3.25)
+    assert np.abs(o1 - o0).max() < 1e-12 and np.abs(l1 - (l0 - 3.25)).max() < 1e-12
+
+
+def test_additive_mask_matches_key_length():
+    """A 0 / -inf mask dropping keys >= L is the key-length mask L."""
+    rng = np.random.default_rng(32)
+    q, k, v = (rng.standard_normal((150, 16)).astype(np.float32) for _ in range(3))
+    mask = np.where(np.arange(150)[None, :] < 97, 0.0, -np.inf)
+    a = sage.emulate_rows(q, k, v, np.arange(150), 0.25, 64, mask=mask)
+    b = sage.emulate_rows(q, k, v, np.arange(150), 0.25, 64, key_len=97)
+    assert np.array_equal(a, b)

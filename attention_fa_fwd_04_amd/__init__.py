@@ -26,7 +26,7 @@ FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
 EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_fwd_cross", "fa_fwd_strided",
             "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk",
             "fa_fwd_int8qk_pv16_workspace_bytes", "fa_fwd_int8qk_pv16",
-            "fa_merge", "fa_mfma_probe", "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
+            "fa_merge", "fa_mfma_probe", "fa_cvt_probe", "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
 
 class FAUnavailable(RuntimeError):
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
     h.fa_merge.restype = i32
     h.fa_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
     h.fa_mfma_probe.restype = i32
+    h.fa_cvt_probe.argtypes = [i32, vp, vp, ctypes.c_int64, vp]
+    h.fa_cvt_probe.restype = i32
     h.fa_int8qk_kv_block.argtypes = []
     h.fa_int8qk_kv_block.restype = i32
     h.fa_status_string.argtypes = [i32]
@@ -155,6 +157,10 @@ def fa_merge(o_a, lse_a, o_b, lse_b, o, lse, B, H, N, D, dtype, hip_stream) -> i
 
 def fa_mfma_probe(kind, workgroups, iters, out, hip_stream) -> int:
     return lib().fa_mfma_probe(kind, workgroups, iters, out, hip_stream)
+
+
+def fa_cvt_probe(kind, inp, out, n, hip_stream) -> int:
+    return lib().fa_cvt_probe(kind, inp, out, n, hip_stream)
 
 
 PROBE_FLOPS = {0: 2.0 * 32 * 32 * 16, 1: 2.0 * 32 * 32 * 64, 2: 2.0 * 32 * 32 * 32}
@@ -339,11 +345,12 @@ def fwd(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
     return (o, lse) if return_lse else o
 
 
-def fwd_int8qk(q, k, v, *, key_len=None, scale: Optional[float] = None,
+def fwd_int8qk(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
                return_lse: bool = False, workspace=None, out=None, pv: str = "fp8"):
     """The INT8-QK variant for GPU tensors [B, H, N, 128] (bf16 / fp16): P V
     in FP8 (pv="fp8", fa_fwd_int8qk) or in the input's 16-bit type
-    (pv="16", fa_fwd_int8qk_pv16)."""
+    (pv="16", fa_fwd_int8qk_pv16).  Masks as for fwd (additive or boolean
+    attn_mask broadcastable to [B, H, N, N], or key_len [B])."""
     import torch
     if pv not in ("fp8", "16"):
         raise ValueError('pv must be "fp8" or "16"')
@@ -357,7 +364,7 @@ def fwd_int8qk(q, k, v, *, key_len=None, scale: Optional[float] = None,
     need = size_fn(B, H, N, D)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
     keep = []
-    m = _mask_struct(q, None, key_len, keep)
+    m = _mask_struct(q, attn_mask, key_len, keep)
     st = torch.cuda.current_stream(q.device).cuda_stream
     rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                lse.data_ptr() if lse is not None else None,

@@ -404,27 +404,27 @@ int int8qk_common(bool pv16, const void* q, const void* k, const void* v, void* 
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (D != 128) return FA_ERR_UNSUPPORTED;
   const int kind = mask ? mask->kind : FA_MASK_NONE;
-  if (kind == FA_MASK_ADDITIVE) return FA_ERR_UNSUPPORTED;
   if ((int64_t)(N + 256) * D * 2 > (int64_t)UINT32_MAX) return FA_ERR_SHAPE;
   const fa::Int8Layout lay = fa::int8qk_workspace_layout(B, H, N, D, pv16);
   if (!workspace) return FA_ERR_WORKSPACE;
   if (workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
-  const int* key_len = (kind == FA_MASK_KEYLEN) ? static_cast<const int*>(mask->ptr) : nullptr;
+  fa::MaskArgs m{nullptr, 0, 0, 0, 0};
+  if (kind != FA_MASK_NONE) m = fa::MaskArgs{mask->ptr, mask->stride_b, mask->stride_h, mask->stride_q, mask->stride_k};
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (log_enabled())
-    std::fprintf(stderr, "[fa] %s dtype=%s D=%d keylen=%d B=%d H=%d N=%d ws=%zu\n",
-                 name, dtype_name(dtype), D, key_len != nullptr, B, H, N, lay.total);
+    std::fprintf(stderr, "[fa] %s dtype=%s D=%d mask=%d B=%d H=%d N=%d ws=%zu\n",
+                 name, dtype_name(dtype), D, kind, B, H, N, lay.total);
   if (pv16) {
     if (dtype == FA_BF16)
-      rc = fa::launch_int8qk_pv16<__bf16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+      rc = fa::launch_int8qk_pv16<__bf16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, st);
     else
-      rc = fa::launch_int8qk_pv16<_Float16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+      rc = fa::launch_int8qk_pv16<_Float16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, st);
   } else {
     if (dtype == FA_BF16)
-      rc = fa::launch_int8qk<__bf16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+      rc = fa::launch_int8qk<__bf16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, st);
     else
-      rc = fa::launch_int8qk<_Float16>(q, k, v, o, lse, key_len, B, H, N, scale, workspace, lay, st);
+      rc = fa::launch_int8qk<_Float16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, st);
   }
   if (rc != FA_OK) return rc;
   return record_launch(name);
@@ -509,6 +509,29 @@ FA_API int fa_mfma_probe(int kind, int workgroups, int iters, float* out, void* 
   return record_launch("fa_mfma_probe_kernel");
 }
 
+FA_API int fa_cvt_probe(int kind, const float* in, void* out, int64_t n, void* hip_stream) {
+  if (!in || !out) return FA_ERR_NULL;
+  if (n <= 0 || n % 4 != 0 || n / 4 > (int64_t)INT32_MAX * 256) return FA_ERR_SHAPE;
+  if (!aligned(in, 16) || !aligned(out, 8)) return FA_ERR_ALIGN;
+  const int64_t quads = n / 4;
+  const unsigned blocks = (unsigned)((quads + 255) / 256);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  switch (kind) {
+    case fa::kCvtE4m3:
+      hipLaunchKernelGGL((fa::fa_cvt_probe_kernel<fa::kCvtE4m3>), dim3(blocks), dim3(256), 0, st, in, out, quads);
+      break;
+    case fa::kCvtBf16:
+      hipLaunchKernelGGL((fa::fa_cvt_probe_kernel<fa::kCvtBf16>), dim3(blocks), dim3(256), 0, st, in, out, quads);
+      break;
+    case fa::kCvtF16:
+      hipLaunchKernelGGL((fa::fa_cvt_probe_kernel<fa::kCvtF16>), dim3(blocks), dim3(256), 0, st, in, out, quads);
+      break;
+    default:
+      return FA_ERR_ARG;
+  }
+  return record_launch("fa_cvt_probe_kernel");
+}
+
 FA_API int fa_int8qk_kv_block(void) { return fa::kInt8Bc; }
 
 FA_API const char* fa_status_string(int status) {
@@ -527,6 +550,6 @@ FA_API const char* fa_status_string(int status) {
 
 FA_API const char* fa_last_hip_error(void) { return g_hip_err; }
 
-FA_API int fa_abi_version(void) { return 2; }
+FA_API int fa_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -80,6 +80,15 @@ template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
+// Four floats -> four OCP e4m3fn bytes in one dword, round to nearest even
+// (the hardware conversion of the quantised kernels, for 448 P and for V;
+// inputs stay within +-448 (1 + 2^-22) there).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 // 16 bytes of operand from 16/sizeof(T) consecutive floats.
 template <typename T> __device__ __forceinline__ u32x4 pack_chunk(const float* p) {
   u32x4 r;

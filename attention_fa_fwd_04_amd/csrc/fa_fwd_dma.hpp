@@ -160,7 +160,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
       const int r = 32 * G + ln;
       return *reinterpret_cast<const u32x4*>(kb + r * C::ROW + (((2 * st + lh) ^ k_swz(r)) << 4));
     };
-#ifndef FA_DMA_NOPREF
 #pragma unroll
     for (int st = 0; st < C::QKS; ++st) ka[st] = kread(0, st);
     __builtin_amdgcn_sched_barrier(0);
@@ -176,16 +175,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-#else
-    (void)ka;
-#pragma unroll
-    for (int G = 0; G < C::SB; ++G) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[G][i] = 0.f;
-#pragma unroll
-      for (int st = 0; st < C::QKS; ++st) s[G] = mfma_chunk<T>(kread(G, st), qreg[st], s[G]);
-    }
-#endif
 
     if constexpr (MASKED) {
 #pragma unroll

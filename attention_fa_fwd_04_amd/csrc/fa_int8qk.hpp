@@ -276,11 +276,11 @@ __global__ __launch_bounds__(256) void int8_v16t_kernel(
 // LDS by buffer-load DMA into unpadded, chunk-swizzled rows (no staging
 // registers or LDS stores; the operand reads are conflict-free).
 
-template <typename T, int MASKLEN>
+template <typename T, int MASK>
 __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
     const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
-    const int* __restrict__ key_len, T* __restrict__ O, float* __restrict__ LSE,
+    MaskArgs mask, T* __restrict__ O, float* __restrict__ LSE,
     int H, int N, int npad, int groups, int nqt, float c_log2) {
   constexpr int D = 128, BC = kInt8Bc, BR = 128, NT = 256;
   constexpr int KSTR = D;                       // int8 K row (128 bytes, chunks swizzled)
@@ -292,11 +292,11 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   const int ln = lane & 31, lh = lane >> 5;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt, qt = logical - bh * nqt;
-  const int b = bh / H;
+  const int b = bh / H, h = bh - b * H;
 
   int n_eff = N;
-  if constexpr (MASKLEN) {
-    const int L = key_len[b];
+  if constexpr (MASK == kMaskLen) {
+    const int L = reinterpret_cast<const int*>(mask.ptr)[b];
     n_eff = L < 0 ? 0 : (L > N ? N : L);
   }
   const int ntiles = (n_eff + BC - 1) / BC;
@@ -315,6 +315,11 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   // every query of a wave lies in one 64-token scale block
   const float sq_w = sq[(size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)];
   const float* skh = sk + (size_t)bh * groups;
+  // additive mask: this lane's query row (row 0 stands in for rows past N,
+  // whose results are not stored)
+  const float* mrow = nullptr;
+  if constexpr (MASK == kMaskAdd)
+    mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh + (int64_t)(q_ok ? q_row : 0) * mask.sq;
 
   // Tiles reach LDS by buffer-load DMA (1 KB per instruction, two K and two
   // V instructions per wave and tile).  Rows are unpadded; the lane landing
@@ -358,6 +363,18 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     const uint8_t* vb = kb + KBYTES;
     const int kv0 = j * BC;
     const float c = sq_w * skh[j] * c_log2;       // one K scale block per tile
+    // additive mask values of this lane's 32 keys (log2 units), loaded ahead
+    // of the MFMAs; keys past N drop out
+    float madd[32];
+    if constexpr (MASK == kMaskAdd) {
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
+          madd[16 * G + i] = key < N ? mrow[(int64_t)key * mask.sk] * kLog2e : -INFINITY;
+        }
+    }
 
     i32x16 si[2];
 #pragma unroll
@@ -374,7 +391,8 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     }
     // Full tiles: the row max is taken on the exact int32 sums and scaled once
     // (the tile's scale c is >= 0), and the scale is folded into the exp2 FMA.
-    // The ragged last tile scales first so dropped keys can be -inf.
+    // The ragged last tile, and every tile under an additive mask, scales
+    // first (then adds the mask) so dropped keys can be -inf.
     float s[32];
     float mx;
     if constexpr (MASKED) {
@@ -383,7 +401,10 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          s[16 * G + i] = key < n_eff ? (float)si[G][i] * c : -INFINITY;
+          if constexpr (MASK == kMaskAdd)
+            s[16 * G + i] = __builtin_fmaf((float)si[G][i], c, madd[16 * G + i]);
+          else
+            s[16 * G + i] = key < n_eff ? (float)si[G][i] * c : -INFINITY;
         }
       mx = -INFINITY;
 #pragma unroll
@@ -425,9 +446,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
       const float p2 = pexp(s[i + 2]);
       const float p3 = pexp(s[i + 3]);
       psum += (p0 + p1) + (p2 + p3);
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
-      pk[i >> 2] = (uint32_t)w;
+      pk[i >> 2] = e4m3x4(p0, p1, p2, p3);
     }
     l_run += psum;
     const i32x8 bop = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3],
@@ -449,9 +468,13 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   dma_tile(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  const int nfull = n_eff / BC;
-  for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});
-  if (nfull < ntiles) step(nfull, BoolTag<true>{});
+  if constexpr (MASK == kMaskAdd) {
+    for (int j = 0; j < ntiles; ++j) step(j, BoolTag<true>{});
+  } else {
+    const int nfull = n_eff / BC;
+    for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});
+    if (nfull < ntiles) step(nfull, BoolTag<true>{});
+  }
 
   const float l_tot = wave_sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -478,11 +501,11 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
 // the running max) and V^T read unquantised from the workspace (keys permuted
 // per 32 by v16_pos); P V runs on the 16-bit 32x32x16 MFMA, four per 32
 // channels per 64-key tile.
-template <typename T, int MASKLEN>
+template <typename T, int MASK>
 __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const T* __restrict__ vt,
     const float* __restrict__ sq, const float* __restrict__ sk,
-    const int* __restrict__ key_len, T* __restrict__ O, float* __restrict__ LSE,
+    MaskArgs mask, T* __restrict__ O, float* __restrict__ LSE,
     int H, int N, int npad, int groups, int nqt, float c_log2) {
   constexpr int D = 128, BC = kInt8Bc, BR = 128, NT = 256;
   constexpr int KSTR = D + 16;                  // int8 K row + pad
@@ -494,11 +517,11 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
   const int ln = lane & 31, lh = lane >> 5;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt, qt = logical - bh * nqt;
-  const int b = bh / H;
+  const int b = bh / H, h = bh - b * H;
 
   int n_eff = N;
-  if constexpr (MASKLEN) {
-    const int L = key_len[b];
+  if constexpr (MASK == kMaskLen) {
+    const int L = reinterpret_cast<const int*>(mask.ptr)[b];
     n_eff = L < 0 ? 0 : (L > N ? N : L);
   }
   const int ntiles = (n_eff + BC - 1) / BC;
@@ -517,6 +540,11 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
   // every query of a wave lies in one 64-token scale block
   const float sq_w = sq[(size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)];
   const float* skh = sk + (size_t)bh * groups;
+  // additive mask: this lane's query row (row 0 stands in for rows past N,
+  // whose results are not stored)
+  const float* mrow = nullptr;
+  if constexpr (MASK == kMaskAdd)
+    mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh + (int64_t)(q_ok ? q_row : 0) * mask.sq;
 
   // staging: K tile 64 rows x 8 chunks (2 per thread), V^T tile 128 rows x 8
   // chunks (4 per thread)
@@ -561,6 +589,18 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
     const uint8_t* vb = kb + KBYTES;
     const int kv0 = j * BC;
     const float c = sq_w * skh[j] * c_log2;       // one K scale block per tile
+    // additive mask values of this lane's 32 keys (log2 units), loaded ahead
+    // of the MFMAs; keys past N drop out
+    float madd[32];
+    if constexpr (MASK == kMaskAdd) {
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
+          madd[16 * G + i] = key < N ? mrow[(int64_t)key * mask.sk] * kLog2e : -INFINITY;
+        }
+    }
 
     i32x16 si[2];
 #pragma unroll
@@ -576,7 +616,8 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
     }
     // Full tiles: the row max is taken on the exact int32 sums and scaled once
     // (the tile's scale c is >= 0), and the scale is folded into the exp2 FMA.
-    // The ragged last tile scales first so dropped keys can be -inf.
+    // The ragged last tile, and every tile under an additive mask, scales
+    // first (then adds the mask) so dropped keys can be -inf.
     float s[32];
     float mx;
     if constexpr (MASKED) {
@@ -585,7 +626,10 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          s[16 * G + i] = key < n_eff ? (float)si[G][i] * c : -INFINITY;
+          if constexpr (MASK == kMaskAdd)
+            s[16 * G + i] = __builtin_fmaf((float)si[G][i], c, madd[16 * G + i]);
+          else
+            s[16 * G + i] = key < n_eff ? (float)si[G][i] * c : -INFINITY;
         }
       mx = -INFINITY;
 #pragma unroll
@@ -646,9 +690,13 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
   load_tile(0);
   store_tile(0);
   __syncthreads();
-  const int nfull = n_eff / BC;
-  for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});
-  if (nfull < ntiles) step(nfull, BoolTag<true>{});
+  if constexpr (MASK == kMaskAdd) {
+    for (int j = 0; j < ntiles; ++j) step(j, BoolTag<true>{});
+  } else {
+    const int nfull = n_eff / BC;
+    for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});
+    if (nfull < ntiles) step(nfull, BoolTag<true>{});
+  }
 
   const float l_tot = wave_sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -668,7 +716,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
 }
 
 template <typename T>
-int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse, const int* key_len,
+int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse, int mask_kind, MaskArgs m,
                        int B, int H, int N, float scale, void* workspace, const Int8Layout& L, hipStream_t st) {
   constexpr int D = 128;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -694,17 +742,18 @@ int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, flo
   hipLaunchKernelGGL((int8_v16t_kernel<T, D>), dim3(L.groups, BH), dim3(256), 0, st, V, vt, N, L.npad);
   const int nqt = (N + 127) / 128;
   const int grid = BH * nqt;
-  if (key_len)
-    hipLaunchKernelGGL((fa_int8qk_pv16_kernel<T, 1>), dim3(grid), dim3(256), 0, st, q8, k8, vt, sq, sk, key_len,
-                       static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
-  else
-    hipLaunchKernelGGL((fa_int8qk_pv16_kernel<T, 0>), dim3(grid), dim3(256), 0, st, q8, k8, vt, sq, sk, key_len,
-                       static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, q8, k8, vt, sq, sk, m, static_cast<T*>(o), lse, H, N,
+                       L.npad, L.groups, nqt, scale * kLog2e);
+  };
+  if (mask_kind == kMaskLen) go(fa_int8qk_pv16_kernel<T, kMaskLen>);
+  else if (mask_kind == kMaskAdd) go(fa_int8qk_pv16_kernel<T, kMaskAdd>);
+  else go(fa_int8qk_pv16_kernel<T, kMaskNone>);
   return FA_OK;
 }
 
 template <typename T>
-int launch_int8qk(const void* q, const void* k, const void* v, void* o, float* lse, const int* key_len,
+int launch_int8qk(const void* q, const void* k, const void* v, void* o, float* lse, int mask_kind, MaskArgs m,
                   int B, int H, int N, float scale, void* workspace, const Int8Layout& L, hipStream_t st) {
   constexpr int D = 128;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -730,12 +779,13 @@ int launch_int8qk(const void* q, const void* k, const void* v, void* o, float* l
   hipLaunchKernelGGL((int8_quant_v_kernel<T, D>), dim3(L.groups, BH), dim3(256), 0, st, V, vmul, v8t, N, L.npad);
   const int nqt = (N + 127) / 128;
   const int grid = BH * nqt;
-  if (key_len)
-    hipLaunchKernelGGL((fa_int8qk_kernel<T, 1>), dim3(grid), dim3(256), 0, st, q8, k8, v8t, sq, sk, sv, key_len,
-                       static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
-  else
-    hipLaunchKernelGGL((fa_int8qk_kernel<T, 0>), dim3(grid), dim3(256), 0, st, q8, k8, v8t, sq, sk, sv, key_len,
-                       static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, q8, k8, v8t, sq, sk, sv, m, static_cast<T*>(o), lse, H, N,
+                       L.npad, L.groups, nqt, scale * kLog2e);
+  };
+  if (mask_kind == kMaskLen) go(fa_int8qk_kernel<T, kMaskLen>);
+  else if (mask_kind == kMaskAdd) go(fa_int8qk_kernel<T, kMaskAdd>);
+  else go(fa_int8qk_kernel<T, kMaskNone>);
   return FA_OK;
 }
 

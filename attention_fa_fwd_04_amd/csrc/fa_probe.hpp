@@ -11,6 +11,8 @@
 
 #include "fa_common.hpp"
 
+#include <type_traits>
+
 namespace fa {
 
 enum ProbeKind { kProbeBf16 = 0, kProbeFp8 = 1, kProbeInt8 = 2 };
@@ -91,6 +93,27 @@ __global__ __launch_bounds__(256) void fa_mfma_probe_kernel(float* __restrict__ 
     for (int i = 0; i < 16; ++i) sink += (float)(c0[i] ^ c1[i] ^ c2[i] ^ c3[i]);
   }
   if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = sink;
+}
+
+// Conversion probe: the narrowing conversions of the attention kernels,
+// applied to caller-given floats so their rounding can be checked bit by bit
+// against the format definitions.  Each thread converts four consecutive
+// inputs with the same helper the kernels use: e4m3x4 (kind 0, one byte
+// each), pack2<__bf16> (kind 1) or pack2<_Float16> (kind 2, two bytes each).
+enum CvtKind { kCvtE4m3 = 0, kCvtBf16 = 1, kCvtF16 = 2 };
+
+template <int KIND>
+__global__ __launch_bounds__(256) void fa_cvt_probe_kernel(const float* __restrict__ in, void* __restrict__ out,
+                                                           int64_t quads) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= quads) return;
+  const f32x4 x = *reinterpret_cast<const f32x4*>(in + 4 * i);
+  if constexpr (KIND == kCvtE4m3) {
+    reinterpret_cast<uint32_t*>(out)[i] = e4m3x4(x.x, x.y, x.z, x.w);
+  } else {
+    using T = typename std::conditional<KIND == kCvtBf16, __bf16, _Float16>::type;
+    reinterpret_cast<u32x2*>(out)[i] = u32x2{pack2<T>(x.x, x.y), pack2<T>(x.z, x.w)};
+  }
 }
 
 }  // namespace fa

@@ -78,8 +78,8 @@ enum {
  * Attention forward.
  *   q, k, v  [B,H,N,D] dtype (read)         o   [B,H,N,D] dtype (written)
  *   lse      [B,H,N] float32 or NULL: natural-log log-sum-exp of each row's
- *            scaled, masked scores (essay page, section 3.1: the kernel also
- *            emits the row log-sum-exp), -inf for a fully masked row.
+ *            scaled, masked scores (essay page, section 2.3: the Triton kernel
+ *            also emits the row log-sum-exp), -inf for a fully masked row.
  *   mask     NULL or a descriptor (FA_MASK_NONE is the same as NULL).
  *   scale    multiplies Q.K; must be finite and > 0 (1/sqrt(D) is usual).
  * Supported: dtype F32, F16, BF16; D in {32, 40, 128}; N >= 1 with
@@ -176,9 +176,12 @@ FA_API int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float
  * lse (if requested) is that of the smoothed, quantised scores in step 4: it
  * differs from the unquantised row log-sum-exp by -scale * q . kmean (the
  * per-row constant smoothing removes) plus quantisation error.
- * Same tensor conventions as fa_fwd.  dtype F16 or BF16, D = 128.  Masks:
- * NONE or KEYLEN (keys beyond the length are dropped after quantisation;
- * kmean and the scales still run over all N tokens).
+ * Same tensor conventions as fa_fwd.  dtype F16 or BF16, D = 128.  Masks
+ * act after quantisation (kmean and the scales still run over all N
+ * tokens): KEYLEN drops keys beyond the length; ADDITIVE (strides as in
+ * fa_fwd) adds its float32 value to the dequantised, scaled score of step 4,
+ * before the running max of step 5 (scale, then the mask: case-study page,
+ * section 2.3); a row whose keys are all -inf gives O = 0 and lse = -inf.
  *   workspace        device scratch of at least
  *                    fa_fwd_int8qk_workspace_bytes(B,H,N,D) bytes, 256-byte
  *                    aligned; contents on entry are ignored.  On return it
@@ -254,6 +257,20 @@ FA_API int fa_merge(const void* o_a, const float* lse_a, const void* o_b, const 
  * FA_ERR_ALIGN, FA_ERR_ARG (kind).
  */
 FA_API int fa_mfma_probe(int kind, int workgroups, int iters, float* out, void* hip_stream);
+
+/*
+ * Measurement aid, not part of the attention path: the narrowing
+ * conversions the kernels use, applied to n caller-given floats (n a
+ * multiple of 4), so their rounding can be checked bit by bit.
+ *   kind 0: float -> OCP e4m3fn byte (the quantised kernels' conversion of
+ *           448 P and of V; round to nearest even), out: n bytes;
+ *   kind 1: float -> bf16 (P and O in bf16 paths), out: n uint16;
+ *   kind 2: float -> fp16, out: n uint16.
+ * in: 16-byte aligned device floats; out: 8-byte aligned device memory.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (n <= 0 or not a multiple of 4),
+ * FA_ERR_ALIGN, FA_ERR_ARG (kind).
+ */
+FA_API int fa_cvt_probe(int kind, const float* in, void* out, int64_t n, void* hip_stream);
 
 /* Keys per tile of the quantised variant's online softmax (P is rounded
  * against the running max, so the result depends on this tile size). */

@@ -10,8 +10,8 @@ Sources (page titles and sections):
     FlashAttention figure), scale 1/sqrt(D);
   * essay page "FlashAttention原理与工业实战", section 2.1: boolean masks
     where 0 marks a dropped key; section 2.2: the exact softmax done as a max
-    pass, a sum pass and an output pass; section 3.1: the kernel also emits
-    the row log-sum-exp;
+    pass, a sum pass and an output pass; section 2.3: the Triton kernel also
+    emits the row log-sum-exp;
   * case-study page, section 2.3: the order scale first, then add the mask.
 
 Readings where the pages are silent (each listed in the design notes):

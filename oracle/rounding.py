@@ -39,6 +39,11 @@ def round_bf16(x) -> np.ndarray:
     return bf16_bits_to_f64(f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
 
 
+def f32_to_f16_bits(x) -> np.ndarray:
+    """fp32 -> IEEE binary16 bit patterns (uint16), numpy's correctly rounded cast."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def round_f16(x) -> np.ndarray:
     """Value of x after rounding to IEEE binary16, as float64 (exact)."""
     return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float64)

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_static_queries(lib):
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     assert fa.fa_int8qk_kv_block() % 64 == 0
     assert fa.fa_status_string(0) == "ok"
     for code in range(-7, 0):
@@ -101,8 +101,21 @@ def test_int8qk_validation(lib):
     assert call(ws=None) == fa.FA_ERR_WORKSPACE
     assert call(wsb=ws - 1) == fa.FA_ERR_WORKSPACE
     assert call(ws=P + 16) == fa.FA_ERR_ALIGN
-    add = fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P, 0, 0, 0, 1)
-    assert call(mask=ctypes.byref(add)) == fa.FA_ERR_UNSUPPORTED
+    # additive masks are taken; a malformed descriptor is refused before any launch
+    for m, code in ((fa.fa_mask_t(fa.FA_MASK_ADDITIVE, None, 0, 0, 0, 1), fa.FA_ERR_NULL),
+                    (fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P + 2, 0, 0, 0, 1), fa.FA_ERR_ALIGN),
+                    (fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P, 0, 0, -1, 1), fa.FA_ERR_ARG)):
+        assert call(mask=ctypes.byref(m)) == code
+
+
+def test_cvt_probe_validation(lib):
+    assert fa.fa_cvt_probe(0, None, P, 16, None) == fa.FA_ERR_NULL
+    assert fa.fa_cvt_probe(0, P, None, 16, None) == fa.FA_ERR_NULL
+    assert fa.fa_cvt_probe(1, P, P, 0, None) == fa.FA_ERR_SHAPE
+    assert fa.fa_cvt_probe(1, P, P, 6, None) == fa.FA_ERR_SHAPE
+    assert fa.fa_cvt_probe(2, P + 4, P, 16, None) == fa.FA_ERR_ALIGN
+    assert fa.fa_cvt_probe(2, P, P + 4, 16, None) == fa.FA_ERR_ALIGN
+    assert fa.fa_cvt_probe(3, P, P, 16, None) == fa.FA_ERR_ARG
 
 
 def test_wrapper_refuses_cpu_tensors():
@@ -185,8 +198,8 @@ def test_int8qk_pv16_validation(lib):
     assert call(wsb=fa.fa_fwd_int8qk_workspace_bytes(1, 2, 1000, 128)) == fa.FA_ERR_WORKSPACE
     assert call(ws=P + 16) == fa.FA_ERR_ALIGN
     assert call(N=1 << 24) == fa.FA_ERR_SHAPE
-    add = fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P, 0, 0, 0, 1)
-    assert call(mask=ctypes.byref(add)) == fa.FA_ERR_UNSUPPORTED
+    neg = fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P, -1, 0, 0, 1)
+    assert call(mask=ctypes.byref(neg)) == fa.FA_ERR_ARG
 
 
 def test_fwd_ws_outside_split_domain(lib):

@@ -41,6 +41,9 @@ def test_f16_rounding_matches_torch():
     got = rounding.round_f16(x)
     same = (ref == got) | (np.isnan(ref) & np.isnan(got))
     assert same.all()
+    fin = np.isfinite(x)
+    ref_bits = torch.from_numpy(x[fin]).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(rounding.f32_to_f16_bits(x[fin]), ref_bits)
 
 
 def test_e4m3_decode_all_codes_matches_torch():

@@ -18,8 +18,10 @@ bf16 and 2.06-2.31e-4 for fp16 over every case here, which is the rounding
 noise of those formats) and by rare P codes that round the other way from
 fp32 arithmetic (exp2 in fp32 against exp in fp64).  REL_RMS sits about 20 %
 above the measured noise floor, so a drift of about 0.1 % of |O| (bf16)
-fails; against the rounded emulation only the outputs whose rounding flips
-differ, and REL_RMS_ROUNDED bounds those.
+fails.  Against the emulation rounded to the output type only outputs
+whose rounding flips differ: measured up to 4.9e-4 (bf16) and 1.6e-4
+(fp16; there the e4m3 P codes that round the other way in fp32 are of the
+order of the fp16 ulp), bounded by REL_RMS_ROUNDED about 25 % above.
 """
 import sys
 
@@ -35,7 +37,7 @@ pytestmark = pytest.mark.gpu
 
 HALF_ULP = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
 REL_RMS = {torch.float16: 2.6e-4, torch.bfloat16: 2.0e-3}
-REL_RMS_ROUNDED = {torch.float16: 1.5e-4, torch.bfloat16: 6e-4}
+REL_RMS_ROUNDED = {torch.float16: 2.0e-4, torch.bfloat16: 6e-4}
 COS_EMU = 0.999998
 ROUND = {torch.float16: rounding.round_f16, torch.bfloat16: rounding.round_bf16}
 

@@ -23,7 +23,7 @@ FA_MASK_NONE, FA_MASK_ADDITIVE, FA_MASK_KEYLEN = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
 FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
 
-EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_fwd_cross", "fa_fwd_strided",
+EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_fwd_ws_static", "fa_fwd_cross", "fa_fwd_strided",
             "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk",
             "fa_fwd_int8qk_pv16_workspace_bytes", "fa_fwd_int8qk_pv16",
             "fa_merge", "fa_mfma_probe", "fa_cvt_probe", "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     h.fa_fwd_workspace_bytes.restype = sz
     h.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     h.fa_fwd_ws.restype = i32
+    h.fa_fwd_ws_static.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp]
+    h.fa_fwd_ws_static.restype = i32
     h.fa_fwd_cross.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, i32, f32, i32, vp]
     h.fa_fwd_cross.restype = i32
     sp = ctypes.POINTER(fa_stride_t)
@@ -119,6 +121,10 @@ def fa_fwd_ws(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace, worksp
               hip_stream) -> int:
     return lib().fa_fwd_ws(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace,
                            workspace_bytes, hip_stream)
+
+
+def fa_fwd_ws_static(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream) -> int:
+    return lib().fa_fwd_ws_static(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream)
 
 
 def fa_fwd_cross(q, k, v, o, lse, mask, B, H, Nq, Nk, D, scale, dtype, hip_stream) -> int:

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -327,6 +328,70 @@ int launch_split(const void* q, const void* k, const void* v, void* o, float* ls
 }
 }  // namespace
 
+// ---------------------------------------------------------------- static scratch
+//
+// fa_fwd_ws_static runs fa_fwd_ws's split launch on a library-owned scratch
+// buffer instead of a caller workspace, for callers that cannot allocate
+// device memory.  The split workspace depends only on the number of
+// workgroups (one per CU), so one array sized for kStaticMaxGrid CUs serves
+// every shape.  Each GPU the library runs on holds its own copy of the array
+// until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device.
+namespace {
+constexpr int kStaticMaxGrid = 256;                                    // MI355X compute units
+constexpr size_t kStaticCntBytes = ((size_t)(kStaticMaxGrid + 1) * sizeof(unsigned) + 255) / 256 * 256;
+constexpr size_t kStaticScratchBytes =
+    kStaticCntBytes + (size_t)(kStaticMaxGrid + 1) * 2 * fa::kPartFloats * sizeof(float);   // 69,477,632
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+__global__ __launch_bounds__(256) void fa_clear_u32_kernel(unsigned* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+struct StaticScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+StaticScratchSlot g_static_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array.  The first call on a
+// device looks the address up and queues a clear of the arrival counters on
+// `st` (a fill kernel: the split protocol leaves them at zero after every
+// completed call, so once per device is enough).
+int static_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    std::snprintf(g_hip_err, sizeof(g_hip_err), "fa_fwd_ws_static: no usable current device (%d)", dev);
+    return FA_ERR_HIP;
+  }
+  StaticScratchSlot& slot = g_static_scratch[dev];
+  std::call_once(slot.once, [&] {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess) {
+      const int n = (int)(kStaticCntBytes / sizeof(unsigned));
+      hipLaunchKernelGGL(fa_clear_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, static_cast<unsigned*>(p), n);
+      e = hipGetLastError();
+    }
+    slot.err = e;
+    slot.ptr = e == hipSuccess ? p : nullptr;
+  });
+  if (slot.err != hipSuccess || slot.ptr == nullptr) {
+    std::snprintf(g_hip_err, sizeof(g_hip_err), "fa_fwd_ws_static: scratch set-up on device %d: %s", dev,
+                  hipGetErrorString(slot.err));
+    return FA_ERR_HIP;
+  }
+  *out = slot.ptr;
+  return FA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -380,6 +445,29 @@ FA_API int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (dtype == FA_BF16) return launch_split<__bf16>(q, k, v, o, lse, B, H, N, scale, p, workspace, st);
   return launch_split<_Float16>(q, k, v, o, lse, B, H, N, scale, p, workspace, st);
+}
+
+FA_API int fa_fwd_ws_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                            fa_dtype_t dtype, void* hip_stream) {
+  const int kind = mask ? mask->kind : FA_MASK_NONE;
+  const SplitPlan p = split_plan(B, H, N, D, dtype, kind);
+  if (p.grid == 0)
+    return fa_fwd(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, hip_stream);
+  int rc = check_common(q, k, v, o, lse, mask, B, H, N, D, scale);
+  if (rc != FA_OK) return rc;
+  if (!contiguous_range_ok(N, N, D, dtype)) return FA_ERR_SHAPE;
+  if (p.bytes > kStaticScratchBytes) {
+    std::snprintf(g_hip_err, sizeof(g_hip_err),
+                  "fa_fwd_ws_static: the split needs %zu bytes (%d CUs), the static scratch holds %zu (%d CUs)",
+                  p.bytes, p.grid, kStaticScratchBytes, kStaticMaxGrid);
+    return FA_ERR_WORKSPACE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  void* ws = nullptr;
+  if ((rc = static_scratch(st, &ws)) != FA_OK) return rc;
+  if (dtype == FA_BF16) return launch_split<__bf16>(q, k, v, o, lse, B, H, N, scale, p, ws, st);
+  return launch_split<_Float16>(q, k, v, o, lse, B, H, N, scale, p, ws, st);
 }
 
 FA_API size_t fa_fwd_int8qk_workspace_bytes(int B, int H, int N, int D) {

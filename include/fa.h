@@ -163,6 +163,27 @@ FA_API int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float
                      fa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * fa_fwd_ws without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split runs on a scratch array the
+ * library holds in device memory, 69,477,632 bytes per GPU it runs on, kept
+ * until the process ends; it serves up to 256 compute units (one split
+ * workgroup per CU): on a device with more CUs a shape that takes the split
+ * returns FA_ERR_WORKSPACE (see fa_last_hip_error).  Shapes that do not take
+ * the split run fa_fwd.  The call allocates nothing.  Results are bitwise
+ * those of fa_fwd_ws.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on
+ *   one GPU (different streams, or different host threads, without
+ *   ordering) race on it and give wrong results.  The first call on a
+ *   device looks the array up and queues a clear of its arrival counters on
+ *   hip_stream, so it must not be made under graph capture.
+ * Arguments as fa_fwd_ws without workspace / workspace_bytes.
+ */
+FA_API int fa_fwd_ws_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                            fa_dtype_t dtype, void* hip_stream);
+
+/*
  * INT8-QK / FP8-PV variant (handbook page, section "SageAttention").  Steps:
  *   1. kmean[b,h,:] = token mean of K (float32);
  *   2. Q and K - kmean to INT8, one float32 scale per (b, h, 64-token block),

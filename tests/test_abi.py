@@ -219,3 +219,18 @@ def test_fwd_ws_outside_split_domain(lib):
     assert call(scale=0.0) == fa.FA_ERR_ARG
     assert call(B=0) == fa.FA_ERR_SHAPE
     assert call(q=P + 8) == fa.FA_ERR_ALIGN
+
+
+def test_fwd_ws_static_outside_split_domain(lib):
+    """Shapes the split does not take run fa_fwd, with its validation
+    (decided before any device query, so no GPU is touched)."""
+    def call(**kw):
+        a = dict(q=P, B=1, H=2, N=100, D=40, dtype=fa.FA_F16, scale=0.1, mask=None)
+        a.update(kw)
+        return fa.fa_fwd_ws_static(a["q"], P, P, P, None, a["mask"], a["B"], a["H"], a["N"], a["D"], a["scale"],
+                                   a["dtype"], None)
+    assert call(q=None) == fa.FA_ERR_NULL
+    assert call(D=64) == fa.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == fa.FA_ERR_ARG
+    assert call(B=0) == fa.FA_ERR_SHAPE
+    assert call(q=P + 8) == fa.FA_ERR_ALIGN

@@ -30,11 +30,12 @@
 // reads no LDS), from per-lane offsets computed once.  Group A loads K(t+1)
 // in phase 2t + 1 (first read in phase 2t + 2; it replaces K(t-1), last read
 // in phase 2t - 1) and waits for it before that phase's closing barrier.
-// Group B loads V(t+1) in phase 2t + 2 (first read in phase 2t + 4; it
-// replaces V(t-1), last read in phase 2t + 1) and waits for it before the
-// closing barrier of phase 2t + 3; the transposing V reads of its MFMA phase
-// in between make the compiler wait for it there already, about a phase
-// after the issue.  A prologue loads K(0) with all eight waves; group B loads
+// Group B loads V(t+1) in phase 2t + 2 (it replaces V(t-1), last read in
+// phase 2t + 1) and waits for it before that phase's closing barrier too.
+// Each group reads the first P V step's V operands at the end of its softmax
+// phase, where its wave would otherwise idle at the barrier: group A reads
+// V(t) in phase 2t + 1, group B in phase 2t + 2, both after V(t) landed (end
+// of phase 2t).  A prologue loads K(0) with all eight waves; group B loads
 // V(0) in phase 0.
 //
 // The ragged last tile (keys [nfull BC, n_eff)) is processed first with all
@@ -265,12 +266,35 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
     for (int p = 0; p < PVB; ++p) vaddr[p] = vbase + (((4 * p + 2 * ga + (gt >> 1)) ^ v_swz(r_l)) << 4);
   }
 
+  // V operands of the pending P V: step k (16 keys) in va[k % 2].
+  u32x4 va[2][PVB];
+  auto vread = [&](const uint8_t* vb, auto kk) {
+    constexpr int k = decltype(kk)::value;
+    constexpr int off = (32 * (k >> 1) + 16 * (k & 1)) * C::ROW;
+    static_for<PVB>([&](auto pp) {
+      constexpr int p = decltype(pp)::value;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[p] + off));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[p] + off + 8 * C::ROW));
+      va[k % 2][p].x = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
+      va[k % 2][p].y = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
+      va[k % 2][p].z = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
+      va[k % 2][p].w = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
+    });
+  };
+  // The first step's V operands of a phase loop's P V are read at the end of
+  // the preceding softmax phase, whose wave otherwise idles at the barrier:
+  // the V tile is resident by then and no DMA writes that buffer until after
+  // the MFMA phase that uses it.
+  auto vread_first = [&](const uint8_t* vb) { vread(vb, std::integral_constant<int, 0>{}); };
+
   // ---- MFMA phase: O^T += V^T P^T for the previous tile, then S^T = K Q^T
   // for this one.  P V runs first so the narrowed P is dead before S is
   // produced; twelve of the sixteen K operands of Q K^T are read during the
-  // P V steps, the V operands one step ahead of their MFMAs.
-  auto mma_phase = [&](const uint8_t* kb, const uint8_t* vb, auto do_pv, auto do_qk) {
+  // P V steps, the V operands one step ahead of their MFMAs (the first step's
+  // already in va[0] when PRE).
+  auto mma_phase = [&](const uint8_t* kb, const uint8_t* vb, auto do_pv, auto do_qk, auto pre_tag) {
     constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
+    constexpr bool PRE = decltype(pre_tag)::value;
     constexpr int KCH = SB * QKS;                     // K operand chunks per tile
     u32x4 ka[KCH];
     auto kread = [&](int c) {                         // chunk c = st * SB + G
@@ -278,26 +302,12 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
       ka[c] = *reinterpret_cast<const u32x4*>(kb + k_lane + 32 * G * C::ROW + (((2 * st) ^ ky) << 4));
     };
     if constexpr (PV) {
-      u32x4 va[2][PVB];
-      auto vread = [&](auto kk) {
-        constexpr int k = decltype(kk)::value;
-        constexpr int off = (32 * (k >> 1) + 16 * (k & 1)) * C::ROW;
-        static_for<PVB>([&](auto pp) {
-          constexpr int p = decltype(pp)::value;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[p] + off));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[p] + off + 8 * C::ROW));
-          va[k % 2][p].x = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
-          va[k % 2][p].y = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
-          va[k % 2][p].z = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
-          va[k % 2][p].w = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
-        });
-      };
       constexpr int KSTEPS = 2 * SB;
       constexpr int KPER = (KCH - 4) / KSTEPS;         // K chunks read per P V step
-      vread(std::integral_constant<int, 0>{});
+      if constexpr (!PRE) vread(vb, std::integral_constant<int, 0>{});
       static_for<KSTEPS>([&](auto kk) {
         constexpr int k = decltype(kk)::value;
-        if constexpr (k + 1 < KSTEPS) vread(std::integral_constant<int, k + 1>{});
+        if constexpr (k + 1 < KSTEPS) vread(vb, std::integral_constant<int, k + 1>{});
         if constexpr (QK) {
 #pragma unroll
           for (int c = k * KPER; c < (k + 1) * KPER; ++c) kread(c);
@@ -384,9 +394,9 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
     dma(vr, vbuf0, nfull, wave * KB_ALL, KB_ALL, true);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    mma_phase(kbuf0, vbuf0, BoolTag<false>{}, BoolTag<true>{});
+    mma_phase(kbuf0, vbuf0, BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
     softmax_phase(nfull, BoolTag<true>{});
-    mma_phase(kbuf0, vbuf0, BoolTag<true>{}, BoolTag<false>{});
+    mma_phase(kbuf0, vbuf0, BoolTag<true>{}, BoolTag<false>{}, BoolTag<false>{});
     __syncthreads();
   }
 
@@ -421,7 +431,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (kb4 + i) * 1024), 16, o[i] + row_off, 0, 0, 0);
     };
     if (grp == 0) {
-      mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{});
+      mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
       lds_barrier();                                            // phase 0
       for (int t = 0; t + 1 < nt; ++t) {
         // phase 2t + 1: K(t + 1), first read in phase 2t + 2, replaces K(t - 1),
@@ -429,34 +439,38 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
         dma4(kr, kbuf(t + 1), t + 1, ks, offs);
         softmax_phase(t, BoolTag<false>{});
         __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
+        vread_first(vbuf(t));                                   // V(t): landed in phase 2t
         lds_barrier();                                          // phase 2t + 1
-        mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{});
+        mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
         lds_barrier();                                          // phase 2t + 2
       }
       softmax_phase(nt - 1, BoolTag<false>{});
+      vread_first(vbuf(nt - 1));
       lds_barrier();                                            // phase 2nt - 1
-      mma_phase(kbuf(0), vbuf(nt - 1), BoolTag<true>{}, BoolTag<false>{});
+      mma_phase(kbuf(0), vbuf(nt - 1), BoolTag<true>{}, BoolTag<false>{}, BoolTag<true>{});
       lds_barrier();                                            // phase 2nt
       lds_barrier();                                            // phase 2nt + 1
     } else {
       dma4(vr, vbuf(0), 0, vs, offs);                           // V(0), buffer unused yet
       lds_barrier();                                            // phase 0
-      mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{});
+      mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
       __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): V(0) landed
       lds_barrier();                                            // phase 1
       for (int t = 0; t + 1 < nt; ++t) {
-        // phase 2t + 2: V(t + 1), first read in phase 2t + 4, replaces V(t - 1),
-        // last read in phase 2t + 1
+        // phase 2t + 2: V(t + 1), first read at the end of phase 2t + 3,
+        // replaces V(t - 1), last read in phase 2t + 1
         dma4(vr, vbuf(t + 1), t + 1, vs, offs);
         softmax_phase(t, BoolTag<false>{});
-        lds_barrier();                                          // phase 2t + 2
-        mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{});
         __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): V(t + 1) landed
+        vread_first(vbuf(t));
+        lds_barrier();                                          // phase 2t + 2
+        mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
         lds_barrier();                                          // phase 2t + 3
       }
       softmax_phase(nt - 1, BoolTag<false>{});
+      vread_first(vbuf(nt - 1));
       lds_barrier();                                            // phase 2nt
-      mma_phase(kbuf(0), vbuf(nt - 1), BoolTag<true>{}, BoolTag<false>{});
+      mma_phase(kbuf(0), vbuf(nt - 1), BoolTag<true>{}, BoolTag<false>{}, BoolTag<true>{});
       lds_barrier();                                            // phase 2nt + 1
     }
   }

@@ -10,18 +10,17 @@ with unquantised attention by cosine >= 0.99 (the stated tolerances).
 
 Those absolute bounds are loose where |O| is small (|O| ~ 0.006 at the
 76112-token shape), so every case also bounds the error relative to the
-emulation: the relative RMS error ||GPU - emu|| / ||emu||, the same against
-the emulation rounded to the output type, and the cosine between GPU and
-emulation.  A correct kernel differs from the float64 emulation by the
-rounding of O to the output type (measured 1.64-1.68e-3 relative RMS for
-bf16 and 2.06-2.31e-4 for fp16 over every case here, which is the rounding
-noise of those formats) and by rare P codes that round the other way from
-fp32 arithmetic (exp2 in fp32 against exp in fp64).  REL_RMS sits about 20 %
-above the measured noise floor, so a drift of about 0.1 % of |O| (bf16)
-fails.  Against the emulation rounded to the output type only outputs
-whose rounding flips differ: measured up to 4.9e-4 (bf16) and 1.6e-4
-(fp16; there the e4m3 P codes that round the other way in fp32 are of the
-order of the fp16 ulp), bounded by REL_RMS_ROUNDED about 25 % above.
+emulation, row by row and over the case.  A correct kernel differs from the
+float64 emulation by the rounding of O to the output type (per-row relative
+RMS 1.64-1.68e-3 for bf16 and 2.06-2.31e-4 for fp16, measured over every
+case here: the rounding noise of those formats) and by rare e4m3 codes of
+448 P that round the other way because the kernel decides them from an fp32
+exp2 and the emulation from an fp64 exp.  Such a flip moves one row (at small
+N by up to ~1e-2 of |O|, visible above the fp16 noise); a wrong scale,
+dropped tile or misplaced key moves every row.  So: the median per-row
+relative RMS error sits within about 20 % of the rounding noise (ROW_MEDIAN),
+at most 1 % of rows exceed five times that, and the relative RMS error over
+the whole case and the cosine leave room for the flips (REL_RMS, COS_EMU).
 """
 import sys
 
@@ -36,26 +35,30 @@ from oracle import attention, rounding, sage
 pytestmark = pytest.mark.gpu
 
 HALF_ULP = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
-REL_RMS = {torch.float16: 2.6e-4, torch.bfloat16: 2.0e-3}
-REL_RMS_ROUNDED = {torch.float16: 2.0e-4, torch.bfloat16: 6e-4}
-COS_EMU = 0.999998
-ROUND = {torch.float16: rounding.round_f16, torch.bfloat16: rounding.round_bf16}
+ROW_MEDIAN = {torch.float16: 2.6e-4, torch.bfloat16: 2.0e-3}
+REL_RMS = {torch.float16: 8e-4, torch.bfloat16: 2.5e-3}
+COS_EMU = 0.999996
 
 
 def check_vs_emulation(got, ref, tdt, what):
-    """Relative RMS error and cosine of the GPU output against the float64
-    emulation, and the relative RMS error against the emulation rounded to
-    the output type (rows with every key masked are exactly 0 on both sides)."""
-    g, r = np.asarray(got, dtype=np.float64).ravel(), np.asarray(ref, dtype=np.float64).ravel()
-    rr = ROUND[tdt](r)
-    den = max((r * r).sum(), 1e-300)
-    rel = np.sqrt(((g - r) ** 2).sum() / den)
-    rel_r = np.sqrt(((g - rr) ** 2).sum() / den)
-    cos = (g @ r) / max(np.linalg.norm(g) * np.linalg.norm(r), 1e-300)
-    say(f"  {what}: relRMS vs emulation {rel:.3e}, vs rounded emulation {rel_r:.3e}, "
+    """Per-row and whole-case relative RMS error and cosine of the GPU output
+    against the float64 emulation (rows with every key masked are exactly 0
+    on both sides and are left out of the per-row statistics)."""
+    g = np.asarray(got, dtype=np.float64).reshape(-1, 128)
+    r = np.asarray(ref, dtype=np.float64).reshape(-1, 128)
+    rn = np.sqrt((r * r).sum(axis=1))
+    live = rn > 0
+    assert np.all(g[~live] == 0), what
+    row = np.sqrt(((g - r) ** 2).sum(axis=1))[live] / rn[live]
+    med = float(np.median(row)) if row.size else 0.0
+    bad = float((row > 5 * ROW_MEDIAN[tdt]).mean()) if row.size else 0.0
+    rel = np.sqrt(((g - r) ** 2).sum() / max((r * r).sum(), 1e-300))
+    cos = (g.ravel() @ r.ravel()) / max(np.linalg.norm(g) * np.linalg.norm(r), 1e-300)
+    say(f"  {what}: per-row relRMS median {med:.3e} (rows > 5x bound: {bad:.2%}), relRMS {rel:.3e}, "
         f"cosine vs emulation {cos:.7f}")
+    assert med <= ROW_MEDIAN[tdt], what
+    assert bad <= 0.01, what
     assert rel <= REL_RMS[tdt], what
-    assert rel_r <= REL_RMS_ROUNDED[tdt], what
     assert cos >= COS_EMU, what
 
 
@@ -146,7 +149,7 @@ def test_quantised_operands_bit_exact(dev, dt):
 @pytest.mark.parametrize("keylen", [False, True])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_int8qk_parity_small(dev, dt, keylen):
-    for N in (1, 63, 64, 65, 200, 1000):
+    for N in (1, 63, 64, 65, 127, 128, 129, 200, 1000):
         w = Workload(95, f"int8-{dt}", dt, 2, 2, N, 128, k_offset_var=2.0)
         inp = make_inputs(w)
         kl = torch.tensor([max(1, N // 3), N], dtype=torch.int32) if keylen else None
@@ -327,7 +330,7 @@ def additive_mask(N, seed, B=2):
 @pytest.mark.parametrize("pv", ["fp8", "16"])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_additive_mask_parity(dev, dt, pv):
-    for N in (1, 63, 64, 65, 200, 1000):
+    for N in (1, 63, 64, 65, 129, 200, 1000):
         w = Workload(99, f"int8-add-{dt}", dt, 2, 2, N, 128, k_offset_var=2.0)
         inp = make_inputs(w)
         mv = additive_mask(N, 1000 + N)

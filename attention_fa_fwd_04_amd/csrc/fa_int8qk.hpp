@@ -2,16 +2,16 @@
 // section "SageAttention": K smoothed by its mean, Q and K quantised to INT8
 // so Q K^T runs on integer matrix cores, P and V in FP8).
 //
-// Four prepass launches and the main kernel, all on the caller's stream:
+// Three prepass launches and the main kernel, all on the caller's stream:
 //   int8_stats      per (b,h, 512-token split): float64 partial sums of K and
 //                   partial max |V| per channel (fixed order, no atomics)
 //   int8_finalize   per (b,h): kmean = fp32(sum / N); V scale av/448 and 448/av
-//   int8_quant_qk   per (b,h, 64-token block, Q or K): X = Q or fp32(K - kmean),
-//                   a = max |X|, codes rint(fp32(X * fp32(127/a))) in [-127,127],
-//                   scale fp32(a/127)
-//   int8_quant_v    per (b,h, 64-token block): e4m3(fp32(V * fp32(448/av))),
-//                   written transposed as V^T[d][key] with the key order of
-//                   each 64-key group permuted to match the P operand
+//   int8_quant      per (b,h, 64-token block) and per Q, K, V:
+//                   Q / K: X = Q or fp32(K - kmean), a = max |X|, codes
+//                   rint(fp32(X * fp32(127/a))) in [-127,127], scale fp32(a/127);
+//                   V: e4m3(fp32(V * fp32(448/av))), written transposed as
+//                   V^T[d][key] with the key order of each 64-key group
+//                   permuted to match the P operand
 //   fa_int8qk       the online-softmax loop: S = (Q8 K8^T) * sq * sk * scale
 //                   from exact int32 sums; P against the exact running max
 //                   (no lazy rescale: P <= 1 is what makes the x448 FP8 scale
@@ -137,16 +137,14 @@ __global__ __launch_bounds__(128) void int8_finalize_kernel(
   vmul[(size_t)bh * D + d] = m > 0.f ? 448.f / m : 0.f;
 }
 
-// One 64-token block of Q (blockIdx.z == 0) or K - kmean (blockIdx.z == 1).
+// One 64-token block of Q (isk == 0) or K - kmean (isk == 1), 256 threads.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void int8_quant_qk_kernel(
+__device__ __forceinline__ void quant_qk_block(
     const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ kmean,
     int8_t* __restrict__ q8, int8_t* __restrict__ k8, float* __restrict__ sq, float* __restrict__ sk,
-    int N, int npad, int groups) {
+    int N, int npad, int groups, int g, int bh, int isk, float* wmax) {
   static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
   constexpr int CH = D / 8;
-  __shared__ float wmax[4];
-  const int g = blockIdx.x, bh = blockIdx.y, isk = blockIdx.z;
   const T* X = (isk ? K : Q) + (size_t)bh * N * D;
   int8_t* X8 = (isk ? k8 : q8) + (size_t)bh * npad * D;
   const int t = threadIdx.x;
@@ -159,10 +157,16 @@ __global__ __launch_bounds__(256) void int8_quant_qk_kernel(
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (row < N) raw = *reinterpret_cast<const u32x4*>(X + (size_t)row * D + c * 8);
     const T* v = reinterpret_cast<const T*>(&raw);
+    float km[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (isk && row < N) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(kmean + (size_t)bh * D + c * 8);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(kmean + (size_t)bh * D + c * 8 + 4);
+      km[0] = lo.x; km[1] = lo.y; km[2] = lo.z; km[3] = lo.w;
+      km[4] = hi.x; km[5] = hi.y; km[6] = hi.z; km[7] = hi.w;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float f = (float)v[e];
-      if (isk && row < N) f = f - kmean[(size_t)bh * D + c * 8 + e];
+      const float f = (float)v[e] - km[e];
       x[i][e] = f;
       a = fmaxf(a, fabsf(f));
     }
@@ -188,43 +192,52 @@ __global__ __launch_bounds__(256) void int8_quant_qk_kernel(
   if (t == 0) (isk ? sk : sq)[(size_t)bh * groups + g] = a > 0.f ? a / 127.f : 0.f;
 }
 
-// One 64-token block of V -> e4m3, transposed into V^T[d][64g + v8_pos(k)].
+// One 64-token block of V -> e4m3, transposed into V^T[d][64g + v8_pos(k)]
+// (keys >= N are zero), 256 threads.  Thread t converts keys 4m .. 4m+3
+// (m = t % 16) of channels 8c .. 8c+7 (c = t / 16); v8_pos keeps 4
+// consecutive keys in consecutive positions, so each channel's 4 bytes are
+// one dword LDS store.  LDS rows of 72 bytes put the four channel groups of
+// a wave (8 channels apart) in disjoint 16-bank ranges: the stores are
+// conflict-free.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void int8_quant_v_kernel(
+__device__ __forceinline__ void quant_v_block(
     const T* __restrict__ V, const float* __restrict__ vmul, uint8_t* __restrict__ v8t,
-    int N, int npad) {
+    int N, int npad, int g, int bh, uint8_t* tile) {
   static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
-  constexpr int TS = 64 + 16;                   // LDS row: 64 keys + pad
-  __shared__ __attribute__((aligned(16))) uint8_t tile[D * TS];
-  const int g = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  constexpr int TS = kQBlock + 8;                // LDS row bytes (18 dwords)
+  const int t = threadIdx.x;
   const T* Vh = V + (size_t)bh * N * D;
-  // thread: key k = t / 4, channels 32 * (t % 4) .. +31
-  const int k = t >> 2, c0 = 32 * (t & 3);
-  const int row = g * kQBlock + k;
-  const int pos = v8_pos(k);
+  const float* vm = vmul + (size_t)bh * D;
+  const int m = t & 15, c8 = t >> 4;
+  const f32x4 m0 = *reinterpret_cast<const f32x4*>(vm + 8 * c8);
+  const f32x4 m1 = *reinterpret_cast<const f32x4*>(vm + 8 * c8 + 4);
+  uint32_t word[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int kk = 0; kk < 4; ++kk) {
+    const int row = g * kQBlock + 4 * m + kk;
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (row < N) raw = *reinterpret_cast<const u32x4*>(Vh + (size_t)row * D + c0 + 8 * q);
+    if (row < N) raw = *reinterpret_cast<const u32x4*>(Vh + (size_t)row * D + 8 * c8);
     const T* v = reinterpret_cast<const T*>(&raw);
+    const uint32_t lo = e4m3x4((float)v[0] * m0.x, (float)v[1] * m0.y, (float)v[2] * m0.z, (float)v[3] * m0.w);
+    const uint32_t hi = e4m3x4((float)v[4] * m1.x, (float)v[5] * m1.y, (float)v[6] * m1.z, (float)v[7] * m1.w);
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int d = c0 + 8 * q + e;
-      const float y0 = (float)v[e] * vmul[(size_t)bh * D + d];
-      const float y1 = (float)v[e + 1] * vmul[(size_t)bh * D + d + 1];
-      const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-      tile[d * TS + pos] = (uint8_t)(pk & 0xFF);
-      tile[(d + 1) * TS + pos] = (uint8_t)((pk >> 8) & 0xFF);
+    for (int e = 0; e < 4; ++e) {
+      word[e] |= ((lo >> (8 * e)) & 0xFFu) << (8 * kk);
+      word[4 + e] |= ((hi >> (8 * e)) & 0xFFu) << (8 * kk);
     }
   }
+  const int pos = v8_pos(4 * m);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(tile + (8 * c8 + e) * TS + pos) = word[e];
   __syncthreads();
-  // thread: channel d = t / 2, 32 positions (t % 2)
+  // thread: channel d = t / 2, 32 positions (t % 2), four 8-byte LDS reads
   const int d = t >> 1, half = t & 1;
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + d * TS + 32 * half);
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + d * TS + 32 * half + 16);
+  u32x2 part[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[i] = *reinterpret_cast<const u32x2*>(tile + d * TS + 32 * half + 8 * i);
   uint8_t* dst = v8t + ((size_t)bh * D + d) * npad + (size_t)g * kQBlock + 32 * half;
-  *reinterpret_cast<u32x4*>(dst) = lo;
-  *reinterpret_cast<u32x4*>(dst + 16) = hi;
+  *reinterpret_cast<u32x4*>(dst) = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
+  *reinterpret_cast<u32x4*>(dst + 16) = u32x4{part[2].x, part[2].y, part[3].x, part[3].y};
 }
 
 // Position of key k (0..31) inside its 32-key block of the 16-bit V^T: the
@@ -238,12 +251,11 @@ __host__ __device__ constexpr int v16_pos(int k) {
 // One 64-token block of V (16-bit, unquantised), transposed into
 // V^T[d][64 g + 32 (k >> 5) + v16_pos(k & 31)]; keys >= N are zero.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void int8_v16t_kernel(
-    const T* __restrict__ V, T* __restrict__ vt, int N, int npad) {
+__device__ __forceinline__ void v16t_block(const T* __restrict__ V, T* __restrict__ vt, int N, int npad, int g,
+                                           int bh, T* tile) {
   static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
   constexpr int TS = 64 + 8;                    // LDS row: 64 keys + pad (elements)
-  __shared__ __attribute__((aligned(16))) T tile[D * TS];
-  const int g = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int t = threadIdx.x;
   const T* Vh = V + (size_t)bh * N * D;
   // thread: key k = t / 4, channels 32 * (t % 4) .. +31
   const int k = t >> 2, c0 = 32 * (t & 3);
@@ -264,6 +276,26 @@ __global__ __launch_bounds__(256) void int8_v16t_kernel(
 #pragma unroll
   for (int c = 0; c < 4; ++c)
     *reinterpret_cast<u32x4*>(dst + 8 * c) = *reinterpret_cast<const u32x4*>(tile + d * TS + 32 * half + 8 * c);
+}
+
+// The quantisation launch: blockIdx = (64-token block, b * H + h, which):
+// which 0 quantises Q, 1 K - kmean (per-block INT8 codes and scales), 2 V
+// (e4m3 V^T, or the 16-bit V^T of the INT8-QK / 16-bit-PV form).
+template <typename T, int D, bool PV16>
+__global__ __launch_bounds__(256) void int8_quant_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ kmean,
+    const float* __restrict__ vmul, int8_t* __restrict__ q8, int8_t* __restrict__ k8, void* __restrict__ vt,
+    float* __restrict__ sq, float* __restrict__ sk, int N, int npad, int groups) {
+  constexpr int VT_BYTES = PV16 ? D * (64 + 8) * 2 : D * (kQBlock + 8);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[VT_BYTES];
+  const int g = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
+  if (which < 2) {
+    quant_qk_block<T, D>(Q, K, kmean, q8, k8, sq, sk, N, npad, groups, g, bh, which, reinterpret_cast<float*>(lds));
+  } else if constexpr (PV16) {
+    v16t_block<T, D>(V, static_cast<T*>(vt), N, npad, g, bh, reinterpret_cast<T*>(lds));
+  } else {
+    quant_v_block<T, D>(V, vmul, static_cast<uint8_t*>(vt), N, npad, g, bh, lds);
+  }
 }
 
 // ---------------------------------------------------------------- main kernel
@@ -737,9 +769,8 @@ int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, flo
   hipLaunchKernelGGL((int8_stats_kernel<T, D>), dim3(L.splits, BH), dim3(256), 0, st, K, V, kpart, vpart, N, L.splits,
                      L.split_rows);
   hipLaunchKernelGGL((int8_finalize_kernel<D>), dim3(BH), dim3(D), 0, st, kpart, vpart, kmean, sv, vmul, N, L.splits);
-  hipLaunchKernelGGL((int8_quant_qk_kernel<T, D>), dim3(L.groups, BH, 2), dim3(256), 0, st, Q, K, kmean, q8, k8, sq, sk,
-                     N, L.npad, L.groups);
-  hipLaunchKernelGGL((int8_v16t_kernel<T, D>), dim3(L.groups, BH), dim3(256), 0, st, V, vt, N, L.npad);
+  hipLaunchKernelGGL((int8_quant_kernel<T, D, true>), dim3(L.groups, BH, 3), dim3(256), 0, st, Q, K, V, kmean, vmul, q8,
+                     k8, static_cast<void*>(vt), sq, sk, N, L.npad, L.groups);
   const int nqt = (N + 127) / 128;
   const int grid = BH * nqt;
   auto go = [&](auto kernel) {
@@ -774,9 +805,8 @@ int launch_int8qk(const void* q, const void* k, const void* v, void* o, float* l
   hipLaunchKernelGGL((int8_stats_kernel<T, D>), dim3(L.splits, BH), dim3(256), 0, st, K, V, kpart, vpart, N, L.splits,
                      L.split_rows);
   hipLaunchKernelGGL((int8_finalize_kernel<D>), dim3(BH), dim3(D), 0, st, kpart, vpart, kmean, sv, vmul, N, L.splits);
-  hipLaunchKernelGGL((int8_quant_qk_kernel<T, D>), dim3(L.groups, BH, 2), dim3(256), 0, st, Q, K, kmean, q8, k8, sq, sk,
-                     N, L.npad, L.groups);
-  hipLaunchKernelGGL((int8_quant_v_kernel<T, D>), dim3(L.groups, BH), dim3(256), 0, st, V, vmul, v8t, N, L.npad);
+  hipLaunchKernelGGL((int8_quant_kernel<T, D, false>), dim3(L.groups, BH, 3), dim3(256), 0, st, Q, K, V, kmean, vmul,
+                     q8, k8, static_cast<void*>(v8t), sq, sk, N, L.npad, L.groups);
   const int nqt = (N + 127) / 128;
   const int grid = BH * nqt;
   auto go = [&](auto kernel) {

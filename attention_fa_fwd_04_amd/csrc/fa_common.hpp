@@ -84,7 +84,10 @@ template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b
 // (the hardware conversion of the quantised kernels, for 448 P and for V;
 // inputs stay within +-448 (1 + 2^-22) there).
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion fills the low half and keeps the old high half,
+  // which the second overwrites: any old value will do, and a's own bits
+  // (dead after this) let the conversion write in place of a
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }

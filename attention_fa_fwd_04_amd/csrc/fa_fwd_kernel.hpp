@@ -290,7 +290,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
     // P = exp2(S*c - m), row sum
-    float psum = 0.f;
+    float psum = -0.f;                            // -0 + x == x: the first add folds away
 #pragma unroll
     for (int G = 0; G < C::SB; ++G)
 #pragma unroll

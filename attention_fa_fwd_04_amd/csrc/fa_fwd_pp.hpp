@@ -366,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
         for (int i = 0; i < 16; ++i) acc[p][i] *= alpha;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
+    float psum = -0.f;                            // -0 + x == x: the first add folds away
 #pragma unroll
     for (int G = 0; G < SB; ++G)
 #pragma unroll

@@ -298,6 +298,16 @@ __global__ __launch_bounds__(256) void int8_quant_kernel(
   }
 }
 
+// The QK^T accumulators start at the bit pattern of the float 1.5 * 2^23.  An
+// int8 dot product d over D = 128 channels has |d| <= 127 * 127 * 128 < 2^21,
+// so the biased sum is the bit pattern of 1.5 * 2^23 + d, a float in
+// [2^23, 2^24) where floats are spaced 1: one float subtraction recovers d
+// exactly (cheaper than an int-to-float conversion), and the biased sums
+// compare as integers in the order of d.
+constexpr int kAccBias = 0x4B400000;
+constexpr float kAccBiasF = 12582912.f;
+__device__ __forceinline__ float unbias(int a) { return __builtin_bit_cast(float, a) - kAccBiasF; }
+
 // ---------------------------------------------------------------- main kernel
 //
 // Same work split as fa_fwd_kernel: 4 waves x 32 query rows, S^T = K Q^T so a
@@ -412,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) si[G][i] = 0;
+      for (int i = 0; i < 16; ++i) si[G][i] = kAccBias;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int r = 32 * G + ln;
@@ -434,9 +444,9 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
           if constexpr (MASK == kMaskAdd)
-            s[16 * G + i] = __builtin_fmaf((float)si[G][i], c, madd[16 * G + i]);
+            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, madd[16 * G + i]);
           else
-            s[16 * G + i] = key < n_eff ? (float)si[G][i] * c : -INFINITY;
+            s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
         }
       mx = -INFINITY;
 #pragma unroll
@@ -448,9 +458,9 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           imx = max(imx, si[G][i]);
-          s[16 * G + i] = (float)si[G][i];
+          s[16 * G + i] = unbias(si[G][i]);
         }
-      mx = (float)imx * c;
+      mx = unbias(imx) * c;
     }
     mx = wave_max_halves_valu(mx);
     const float m_new = fmaxf(m_run, mx);
@@ -469,7 +479,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     auto pexp = [&](float x) {
       return MASKED ? __builtin_amdgcn_exp2f(x - moff) : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -moff));
     };
-    float psum = 0.f;
+    float psum = -0.f;                            // -0 + x == x: the first add folds away
     uint32_t pk[8];
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
@@ -638,7 +648,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) si[G][i] = 0;
+      for (int i = 0; i < 16; ++i) si[G][i] = kAccBias;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * G + ln) * KSTR + (2 * st + lh) * 16);
@@ -659,9 +669,9 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
           if constexpr (MASK == kMaskAdd)
-            s[16 * G + i] = __builtin_fmaf((float)si[G][i], c, madd[16 * G + i]);
+            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, madd[16 * G + i]);
           else
-            s[16 * G + i] = key < n_eff ? (float)si[G][i] * c : -INFINITY;
+            s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
         }
       mx = -INFINITY;
 #pragma unroll
@@ -673,9 +683,9 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           imx = max(imx, si[G][i]);
-          s[16 * G + i] = (float)si[G][i];
+          s[16 * G + i] = unbias(si[G][i]);
         }
-      mx = (float)imx * c;
+      mx = unbias(imx) * c;
     }
     mx = wave_max_halves_valu(mx);
     const float m_new = fmaxf(m_run, mx);
@@ -693,7 +703,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
     auto pexp = [&](float x) {
       return MASKED ? __builtin_amdgcn_exp2f(x - m_use) : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -m_use));
     };
-    float psum = 0.f;
+    float psum = -0.f;                            // -0 + x == x: the first add folds away
     float pv[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {

@@ -30,6 +30,61 @@ struct MaskArgs {
   int64_t sb, sh, sq, sk;
 };
 
+// True when every query row of the mask is key-contiguous and 16-byte aligned
+// (the same for all lanes: it depends on the kernel arguments only).
+__device__ __forceinline__ bool mask_rows_vec4(const MaskArgs& m) {
+  return m.sk == 1 && ((m.sb | m.sh | m.sq) & 3) == 0 && (reinterpret_cast<uintptr_t>(m.ptr) & 15) == 0;
+}
+
+// Additive-mask values (as stored) of one lane's keys of the key tile at kv0
+// (SB blocks of 32 keys): index 16 G + i holds key kv0 + 32 G + 8 (i >> 2) +
+// 4 lh + (i & 3), the order of the transposed score tile.  Keys at or past nk
+// read -inf.  A whole tile of a vec4 mask row takes 4 SB 16-byte loads,
+// anything else one load per key.  Issued a tile ahead of their use, the
+// loads complete under the current tile's work.
+template <int SB>
+__device__ __forceinline__ void load_mask_tile(float (&dst)[16 * SB], const float* mrow, int64_t sk, bool vec4,
+                                               int kv0, int nk, int lh) {
+  if (vec4 && kv0 + 32 * SB <= nk) {
+#pragma unroll
+    for (int G = 0; G < SB; ++G)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(mrow + kv0 + 32 * G + 8 * g + 4 * lh);
+        dst[16 * G + 4 * g] = x.x;
+        dst[16 * G + 4 * g + 1] = x.y;
+        dst[16 * G + 4 * g + 2] = x.z;
+        dst[16 * G + 4 * g + 3] = x.w;
+      }
+  } else {
+#pragma unroll
+    for (int G = 0; G < SB; ++G)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
+        dst[16 * G + i] = key < nk ? mrow[(int64_t)key * sk] : -INFINITY;
+      }
+  }
+}
+
+// Additive-mask values (as stored) of the 4 consecutive keys key0 .. key0 + 3
+// of one query row; keys at or past nk read -inf.  VEC: the row is
+// key-contiguous and 16-byte aligned and all four keys are below nk, so one
+// 16-byte load does.
+template <bool VEC>
+__device__ __forceinline__ f32x4 mask_quad(const float* mrow, int64_t sk, int key0, int nk) {
+  if constexpr (VEC) {
+    return *reinterpret_cast<const f32x4*>(mrow + key0);
+  } else {
+    f32x4 r;
+    r.x = key0 < nk ? mrow[(int64_t)key0 * sk] : -INFINITY;
+    r.y = key0 + 1 < nk ? mrow[(int64_t)(key0 + 1) * sk] : -INFINITY;
+    r.z = key0 + 2 < nk ? mrow[(int64_t)(key0 + 2) * sk] : -INFINITY;
+    r.w = key0 + 3 < nk ? mrow[(int64_t)(key0 + 3) * sk] : -INFINITY;
+    return r;
+  }
+}
+
 // Element strides of a [B, H, N, D] tensor whose D elements are contiguous:
 // element (b, h, n, d) is at base[b * sb + h * sh + n * sn + d].
 struct RowLayout {

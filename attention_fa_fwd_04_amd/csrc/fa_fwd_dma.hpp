@@ -140,10 +140,14 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
 
   constexpr bool kPre = (MASK == kMaskAdd);
   const float cs = kPre ? 1.f : c_log2;
+  // additive mask: this lane's query row (row 0 stands in for rows past Nq,
+  // whose results are not stored)
   const float* mrow = nullptr;
+  bool mvec = false;
   if constexpr (kPre) {
     mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh +
            (int64_t)(q_ok ? q_row : 0) * mask.sq;
+    mvec = mask_rows_vec4(mask);
   }
 
   auto step = [&](int j, auto masked_tag) {
@@ -177,22 +181,33 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
     }
 
     if constexpr (MASKED) {
+      if constexpr (kPre) {
+        // additive mask, 4 consecutive keys per load (keys past Nk read -inf),
+        // each quad loaded next to its use (the tile's scores hold the
+        // registers); a whole tile of a key-contiguous aligned row takes
+        // 16-byte loads
+        auto add_mask = [&](auto vec_tag) {
+          constexpr bool VEC = decltype(vec_tag)::value;
 #pragma unroll
-      for (int G = 0; G < C::SB; ++G)
+          for (int G = 0; G < C::SB; ++G)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          float t = -INFINITY;
-          if constexpr (kPre) {
-            if (key < Nk) {
-              const float mv = q_ok ? mrow[(int64_t)key * mask.sk] : 0.f;
-              t = __builtin_fmaf(s[G][i], c_log2, mv * kLog2e);
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 mq = mask_quad<VEC>(mrow, mask.sk, kv0 + 32 * G + 8 * g + 4 * lh, Nk);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) s[G][4 * g + r] = __builtin_fmaf(s[G][4 * g + r], c_log2, mq[r] * kLog2e);
             }
-          } else {
-            t = key < n_eff ? s[G][i] : -INFINITY;
+        };
+        if (mvec && kv0 + BC <= Nk) add_mask(BoolTag<true>{});
+        else add_mask(BoolTag<false>{});
+      } else {
+#pragma unroll
+        for (int G = 0; G < C::SB; ++G)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
+            s[G][i] = key < n_eff ? s[G][i] : -INFINITY;
           }
-          s[G][i] = t;
-        }
+      }
     }
     float mx = -INFINITY;
 #pragma unroll

@@ -23,7 +23,7 @@
 // 32-key block (key 8g + 4h + r stored at position 16h + 4g + r), which makes
 // each lane's 16 keys contiguous and 16-byte readable.
 //
-// Memory path.  K rows go to LDS as-is (row stride padded by 16 bytes, which
+// Memory path.  K rows go to LDS as-is (row stride odd in 16-byte units, which
 // keeps the 16-lane phases of ds_read_b128 on distinct banks); V goes through
 // registers, is transposed with byte permutes and written as V^T.  The next
 // K/V tile is fetched into registers while the current one is consumed, and
@@ -45,7 +45,14 @@ struct FwdCfg {
   static constexpr int EPC = 16 / E;              // elements per 16-byte chunk
   static constexpr int DCH = D * E / 16;          // chunks per row
   static constexpr int QKS = (DCH + 1) / 2;       // MFMA steps over D (2 chunks each)
-  static constexpr int KSTR = 32 * QKS + 16;      // K row stride in LDS, bytes
+  // K row stride in LDS, bytes.  A row of an odd number of chunks is stored
+  // unpadded: the stride (odd in 16-byte units) keeps the 16-lane phases of
+  // both the row-per-lane operand reads and the consecutive staging stores on
+  // distinct banks.  The QK step that would read chunk DCH (past the row)
+  // re-reads chunk DCH - 1 instead; its Q chunk is zero, so it adds nothing.
+  // Even chunk counts keep a padded row (16 bytes past the last QK step).
+  static constexpr bool KDENSE = (DCH & 1) != 0;
+  static constexpr int KSTR = KDENSE ? 16 * DCH : 32 * QKS + 16;
   static constexpr int PVB = (D + 31) / 32;       // 32-channel blocks of O^T
   static constexpr int VSTR = BC * E + 16;        // V^T row stride in LDS, bytes
   static constexpr int KBYTES = BC * KSTR;
@@ -113,7 +120,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
 
   // Zero the padding the tile writes never touch: K chunks past D (QK steps
   // are 2 chunks wide) and V^T rows past D (PV blocks are 32 channels).
-  if constexpr (2 * C::QKS > C::DCH) {
+  if constexpr (!C::KDENSE && 2 * C::QKS > C::DCH) {
     for (int r = tid; r < NBUF * BC; r += C::NT) {
       uint8_t* p = smem + (r / BC) * C::BUF + (r % BC) * C::KSTR + C::DCH * 16;
       for (int c = 0; c < (2 * C::QKS - C::DCH) * 16; c += 16)
@@ -212,10 +219,14 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
   // scale is folded into the exp2 argument.
   constexpr bool kPre = (MASK == kMaskAdd);
   const float cs = kPre ? 1.f : c_log2;
+  // additive mask: this lane's query row (row 0 stands in for rows past Nq,
+  // whose results are not stored)
   const float* mrow = nullptr;
+  bool mvec = false;
   if constexpr (kPre) {
     mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh +
            (int64_t)(q_ok ? q_row : 0) * mask.sq;
+    mvec = mask_rows_vec4(mask);
   }
 
   // One K/V tile: scores, online softmax, P V.  MASKED adds the additive
@@ -235,9 +246,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
     // the matrix work.
     f32x16 s[C::SB];
     u32x4 ka[C::QKS];
+    auto kch = [&](int st) { return C::KDENSE ? min(2 * st + lh, C::DCH - 1) : 2 * st + lh; };
 #pragma unroll
     for (int st = 0; st < C::QKS; ++st)
-      ka[st] = *reinterpret_cast<const u32x4*>(kb + ln * C::KSTR + (2 * st + lh) * 16);
+      ka[st] = *reinterpret_cast<const u32x4*>(kb + ln * C::KSTR + kch(st) * 16);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int G = 0; G < C::SB; ++G) {
@@ -247,29 +259,40 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_kernel(
       for (int st = 0; st < C::QKS; ++st) {
         const u32x4 a = ka[st];
         if (G + 1 < C::SB)
-          ka[st] = *reinterpret_cast<const u32x4*>(kb + (32 * (G + 1) + ln) * C::KSTR + (2 * st + lh) * 16);
+          ka[st] = *reinterpret_cast<const u32x4*>(kb + (32 * (G + 1) + ln) * C::KSTR + kch(st) * 16);
         s[G] = mfma_chunk<T>(a, qreg[st], s[G]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 
     if constexpr (MASKED) {
+      if constexpr (kPre) {
+        // additive mask, 4 consecutive keys per load (keys past Nk read -inf),
+        // each quad loaded next to its use (the tile's scores hold the
+        // registers); a whole tile of a key-contiguous aligned row takes
+        // 16-byte loads
+        auto add_mask = [&](auto vec_tag) {
+          constexpr bool VEC = decltype(vec_tag)::value;
 #pragma unroll
-      for (int G = 0; G < C::SB; ++G)
+          for (int G = 0; G < C::SB; ++G)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          float t = -INFINITY;
-          if constexpr (kPre) {
-            if (key < Nk) {
-              const float mv = q_ok ? mrow[(int64_t)key * mask.sk] : 0.f;
-              t = __builtin_fmaf(s[G][i], c_log2, mv * kLog2e);
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 mq = mask_quad<VEC>(mrow, mask.sk, kv0 + 32 * G + 8 * g + 4 * lh, Nk);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) s[G][4 * g + r] = __builtin_fmaf(s[G][4 * g + r], c_log2, mq[r] * kLog2e);
             }
-          } else {
-            t = key < n_eff ? s[G][i] : -INFINITY;
+        };
+        if (mvec && kv0 + BC <= Nk) add_mask(BoolTag<true>{});
+        else add_mask(BoolTag<false>{});
+      } else {
+#pragma unroll
+        for (int G = 0; G < C::SB; ++G)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
+            s[G][i] = key < n_eff ? s[G][i] : -INFINITY;
           }
-          s[G][i] = t;
-        }
+      }
     }
     float mx = -INFINITY;
 #pragma unroll

@@ -360,8 +360,11 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   // additive mask: this lane's query row (row 0 stands in for rows past N,
   // whose results are not stored)
   const float* mrow = nullptr;
-  if constexpr (MASK == kMaskAdd)
+  bool mvec = false;
+  if constexpr (MASK == kMaskAdd) {
     mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh + (int64_t)(q_ok ? q_row : 0) * mask.sq;
+    mvec = mask_rows_vec4(mask);
+  }
 
   // Tiles reach LDS by buffer-load DMA (1 KB per instruction, two K and two
   // V instructions per wave and tile).  Rows are unpadded; the lane landing
@@ -401,22 +404,14 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int buf = j & 1;
     dma_tile(j + 1, buf ^ 1);                     // past the last tile: never read
+    // additive mask values of this lane's 32 keys (keys past N read -inf),
+    // loaded ahead of the MFMAs (measured no faster issued before the DMA)
+    float mk[32];
+    if constexpr (MASK == kMaskAdd) load_mask_tile<2>(mk, mrow, mask.sk, mvec, j * BC, N, lh);
     const uint8_t* kb = smem + buf * BUF;
     const uint8_t* vb = kb + KBYTES;
     const int kv0 = j * BC;
     const float c = sq_w * skh[j] * c_log2;       // one K scale block per tile
-    // additive mask values of this lane's 32 keys (log2 units), loaded ahead
-    // of the MFMAs; keys past N drop out
-    float madd[32];
-    if constexpr (MASK == kMaskAdd) {
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          madd[16 * G + i] = key < N ? mrow[(int64_t)key * mask.sk] * kLog2e : -INFINITY;
-        }
-    }
 
     i32x16 si[2];
 #pragma unroll
@@ -444,7 +439,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
           if constexpr (MASK == kMaskAdd)
-            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, madd[16 * G + i]);
+            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i] * kLog2e);
           else
             s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
         }
@@ -585,8 +580,11 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
   // additive mask: this lane's query row (row 0 stands in for rows past N,
   // whose results are not stored)
   const float* mrow = nullptr;
-  if constexpr (MASK == kMaskAdd)
+  bool mvec = false;
+  if constexpr (MASK == kMaskAdd) {
     mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh + (int64_t)(q_ok ? q_row : 0) * mask.sq;
+    mvec = mask_rows_vec4(mask);
+  }
 
   // staging: K tile 64 rows x 8 chunks (2 per thread), V^T tile 128 rows x 8
   // chunks (4 per thread)
@@ -626,23 +624,16 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
   auto step = [&](int j, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int buf = j & 1;
+    // additive mask values of this lane's 32 keys (keys past N read -inf),
+    // issued before the next tile's loads so that waiting for them does not
+    // wait for those too (loads complete in issue order)
+    float mk[32];
+    if constexpr (MASK == kMaskAdd) load_mask_tile<2>(mk, mrow, mask.sk, mvec, j * BC, N, lh);
     load_tile(j + 1);
     const uint8_t* kb = smem + buf * BUF;
     const uint8_t* vb = kb + KBYTES;
     const int kv0 = j * BC;
     const float c = sq_w * skh[j] * c_log2;       // one K scale block per tile
-    // additive mask values of this lane's 32 keys (log2 units), loaded ahead
-    // of the MFMAs; keys past N drop out
-    float madd[32];
-    if constexpr (MASK == kMaskAdd) {
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          madd[16 * G + i] = key < N ? mrow[(int64_t)key * mask.sk] * kLog2e : -INFINITY;
-        }
-    }
 
     i32x16 si[2];
 #pragma unroll
@@ -669,7 +660,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
           if constexpr (MASK == kMaskAdd)
-            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, madd[16 * G + i]);
+            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i] * kLog2e);
           else
             s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
         }
@@ -677,15 +668,16 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
 #pragma unroll
       for (int i = 0; i < 32; ++i) mx = fmaxf(mx, s[i]);
     } else {
-      int imx = si[0][0];
+      // the max of the exact integer-valued floats (measured faster here than
+      // the integer max, which the FP8 kernel keeps)
 #pragma unroll
       for (int G = 0; G < 2; ++G)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          imx = max(imx, si[G][i]);
-          s[16 * G + i] = unbias(si[G][i]);
-        }
-      mx = unbias(imx) * c;
+        for (int i = 0; i < 16; ++i) s[16 * G + i] = unbias(si[G][i]);
+      float fmx = s[0];
+#pragma unroll
+      for (int i = 1; i < 32; ++i) fmx = fmaxf(fmx, s[i]);
+      mx = fmx * c;
     }
     mx = wave_max_halves_valu(mx);
     const float m_new = fmaxf(m_run, mx);

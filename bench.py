@@ -15,7 +15,8 @@ attention TFLOP/s = 4*B*H*N^2*D / t.  Unless --no-extra is given the line
 also carries, under "extra", the FLUX-1024^2 layer, the SD1.5 768^2 layer
 with its key lengths (nominal and effective rates) and the Wan 2.1 layer
 through the INT8-QK / FP8-PV entry point next to the bf16 kernel (and the
-INT8-QK / 16-bit-PV form) on the same inputs; --extra adds the
+INT8-QK / 16-bit-PV form) on the same inputs, each comparison timed in
+interleaved rounds (medians); --extra adds the
 cross-attention, window-attention and merge workloads.
 """
 from __future__ import annotations
@@ -24,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -244,6 +246,17 @@ def main() -> int:
             call = lambda: fa.fwd(q, k, v, key_len=kl, out=o, split=split)  # noqa: E731
         return timed(call, steps, warmup)
 
+    def interleaved(w, variants, rounds, steps, warmup):
+        """Median event-timed ms of each variant (measure() keyword sets), the
+        variants alternating round by round (order reversed every other round)
+        so that clock drift under load does not favour whichever runs first."""
+        res = [[] for _ in variants]
+        for r in range(rounds):
+            order = range(len(variants)) if r % 2 == 0 else reversed(range(len(variants)))
+            for i in order:
+                res[i].append(measure(w, steps, warmup, **variants[i])[0])
+        return [statistics.median(x) for x in res]
+
     def merge_bytes(w):
         elt = 4 if w.dtype == "f32" else 2
         return 3 * w.B * w.H * w.N * w.D * elt + 3 * w.B * w.H * w.N * 4
@@ -335,8 +348,10 @@ def main() -> int:
     extra = {}
     if not args.no_extra:
         if split:
-            u_ms, _ = measure(w, 20, 3, split=False)
-            extra[w.name + " (fa_fwd, no split)"] = {"ms": round(u_ms, 4), "tflops": round(flops / (u_ms * 1e-3) / 1e12, 2)}
+            s_ms, u_ms = interleaved(w, [{}, {"split": False}], 6, 20, 3)
+            extra[w.name + " (fa_fwd_ws vs fa_fwd, interleaved)"] = {
+                "split_ms": round(s_ms, 4), "no_split_ms": round(u_ms, 4),
+                "no_split_tflops": round(flops / (u_ms * 1e-3) / 1e12, 2)}
         for wid in (2, 3, 5):
             wx = WORKLOADS[wid]
             if wid == args.workload:
@@ -344,24 +359,26 @@ def main() -> int:
             fl = layer_flops(wx)
             big = wx.N > 50000
             steps, warm = (5, 1) if big else (50, 5)
-            e_ms, _ = measure(wx, steps, warm)
-            rec = {"ms": round(e_ms, 4), "tflops": round(fl / (e_ms * 1e-3) / 1e12, 2)}
             if wx.quantised:
-                rec = {"int8qk_ms": rec["ms"], "int8qk_tops": rec["tflops"],
-                       "entry": "fa_fwd_int8qk (prepass kernels included)"}
-                b_ms, _ = measure(wx, steps, warm, quantised=False)
-                rec["bf16_same_inputs_ms"] = round(b_ms, 3)
-                rec["bf16_same_inputs_tflops"] = round(fl / (b_ms * 1e-3) / 1e12, 2)
-                rec["int8qk_speedup_vs_bf16"] = round(b_ms / e_ms, 3)
-                p_ms, _ = measure(wx, steps, warm, pv16=True)
-                rec["int8qk_pv16_ms"] = round(p_ms, 3)
-                rec["int8qk_pv16_tops"] = round(fl / (p_ms * 1e-3) / 1e12, 2)
-                rec["int8qk_pv16_speedup_vs_bf16"] = round(b_ms / p_ms, 3)
+                # the three forms on the same device inputs, interleaved
+                e_ms, b_ms, p_ms = interleaved(wx, [{}, {"quantised": False}, {"pv16": True}], 2, 3, 1)
+                rec = {"int8qk_ms": round(e_ms, 4), "int8qk_tops": round(fl / (e_ms * 1e-3) / 1e12, 2),
+                       "entry": "fa_fwd_int8qk (prepass kernels included)",
+                       "bf16_same_inputs_ms": round(b_ms, 3),
+                       "bf16_same_inputs_tflops": round(fl / (b_ms * 1e-3) / 1e12, 2),
+                       "int8qk_speedup_vs_bf16": round(b_ms / e_ms, 3),
+                       "int8qk_pv16_ms": round(p_ms, 3),
+                       "int8qk_pv16_tops": round(fl / (p_ms * 1e-3) / 1e12, 2),
+                       "int8qk_pv16_speedup_vs_bf16": round(b_ms / p_ms, 3)}
             elif takes_split(wx):
-                rec["entry"] = "fa_fwd_ws"
-                u_ms, _ = measure(wx, steps, warm, split=False)
-                rec["fa_fwd_no_split_ms"] = round(u_ms, 4)
-                rec["fa_fwd_no_split_tflops"] = round(fl / (u_ms * 1e-3) / 1e12, 2)
+                e_ms, u_ms = interleaved(wx, [{}, {"split": False}], 6, steps, warm)
+                rec = {"ms": round(e_ms, 4), "tflops": round(fl / (e_ms * 1e-3) / 1e12, 2), "entry": "fa_fwd_ws",
+                       "fa_fwd_no_split_ms": round(u_ms, 4),
+                       "fa_fwd_no_split_tflops": round(fl / (u_ms * 1e-3) / 1e12, 2),
+                       "timing": "interleaved rounds, medians"}
+            else:
+                e_ms, _ = measure(wx, steps, warm)
+                rec = {"ms": round(e_ms, 4), "tflops": round(fl / (e_ms * 1e-3) / 1e12, 2)}
             if wx.key_len:
                 eff = 4.0 * wx.H * wx.D * wx.N * float(key_lengths(wx).sum())
                 rec["effective_tflops"] = round(eff / (e_ms * 1e-3) / 1e12, 2)

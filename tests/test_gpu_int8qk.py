@@ -32,6 +32,8 @@ import attention_fa_fwd_04_amd as fa
 from attention_fa_fwd_04_amd.workloads import WORKLOADS, Workload, make_inputs, sample_rows
 from oracle import attention, rounding, sage
 
+from gpu_masks import mask_layouts
+
 pytestmark = pytest.mark.gpu
 
 HALF_ULP = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
@@ -375,3 +377,32 @@ def test_additive_mask_full_strides(dev):
     got = o.cpu().double().numpy()
     assert np.abs(got - ref).max() <= 1e-2
     check_vs_emulation(got, ref, torch.bfloat16, "per-head mask")
+
+
+@pytest.mark.parametrize("pv", ["fp8", "16"])
+def test_additive_mask_layouts_int8(dev, pv):
+    """The quantised kernels read every additive-mask layout (aligned rows,
+    unaligned, transposed, broadcast over queries or over keys) to the
+    emulation's result."""
+    N = 200
+    w = Workload(94, "int8-masklayout", "bf16", 2, 2, N, 128, k_offset_var=2.0)
+    inp = make_inputs(w)
+    qn, kn, vn = (inp[n].double().numpy() for n in ("q", "k", "v"))
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    for name, md in mask_layouts(dev, 2, 2, N, 12).items():
+        say(f"case pv={pv} N={N} mask={name} strides={tuple(md.stride())}")
+        o, lse = fa.fwd_int8qk(q, k, v, attn_mask=md, return_lse=True, pv=pv)
+        torch.cuda.synchronize()
+        mref = np.ascontiguousarray(np.broadcast_to(md.cpu().double().numpy(), (2, 2, N, N)))
+        ref, ref_lse = sage.emulate(qn, kn, vn, w.scale, fa.fa_int8qk_kv_block(), return_lse=True,
+                                    pv="fp8" if pv == "fp8" else "bf16", mask=mref)
+        got = o.cpu().double().numpy()
+        err = np.abs(got - ref)
+        say(f"  max|err|={err.max():.3e} mean|err|={err.mean():.3e}")
+        assert np.all(err <= 1e-2 + HALF_ULP[w.torch_dtype] * np.abs(ref))
+        assert err.mean() <= 1e-3
+        check_vs_emulation(got, ref, w.torch_dtype, name)
+        lg = lse.cpu().double().numpy()
+        assert np.array_equal(np.isneginf(lg), np.isneginf(ref_lse))
+        fin = np.isfinite(ref_lse)
+        assert np.abs(lg[fin] - ref_lse[fin]).max() < 1e-4

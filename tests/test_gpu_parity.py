@@ -23,6 +23,8 @@ import attention_fa_fwd_04_amd as fa
 from attention_fa_fwd_04_amd.workloads import WORKLOADS, Workload, make_inputs, sample_rows
 from oracle import attention
 
+from gpu_masks import mask_layouts
+
 pytestmark = pytest.mark.gpu
 
 O_TOL = {torch.float32: (1e-5, None), torch.float16: (1e-2, 1e-3), torch.bfloat16: (1e-2, 1e-3)}
@@ -251,3 +253,22 @@ def test_video_full(dev):
     o, lse = run(dev, inp)
     rows = sample_rows(w, w.sampled_rows)
     _sampled_check(dev, w, o, lse, inp, rows)
+
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f16", 40), ("f32", 32)])
+def test_additive_mask_layouts(dev, dt, D):
+    """Every mask layout gives the oracle's result (the wrapper passes the
+    mask's pointer and strides as they are)."""
+    N = 200                                                    # three whole 64-key tiles and a ragged one
+    w = Workload(93, f"masklayout-{dt}", dt, 2, 2, N, D)
+    inp = make_inputs(w)
+    qn, kn, vn = (inp[n].double().numpy() for n in ("q", "k", "v"))
+    for name, md in mask_layouts(dev, 2, 2, N, 11).items():
+        say(f"case dt={dt} D={D} N={N} mask={name} strides={tuple(md.stride())}")
+        o, lse = fa.fwd(*(inp[n].to(dev) for n in ("q", "k", "v")), attn_mask=md, return_lse=True)
+        torch.cuda.synchronize()
+        mref = np.broadcast_to(md.cpu().double().numpy(), (2, 2, N, N))
+        ref_o, ref_l = attention.naive(qn, kn, vn, w.scale, mask=mref)
+        check_o(o, ref_o, DT[dt], name)
+        check_lse(lse, ref_l, DT[dt], name)

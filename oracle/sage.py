@@ -29,6 +29,16 @@ way on both sides:
     unquantised P), acc = acc * exp(m_{j-1} - m_j) + sum_t e4m3(448 P_t) v8_t.
   * O = acc * sv / (448 l); a row with every key masked gives O = 0.
 
+Q smoothing (``smooth_q=True``, the handbook's "Q and K minus their block
+means"): for each (b, h, 64-token block g) qbar_g = mean of the block's rows
+of Q that exist (rows < N), summed in float64, divided by their count and
+rounded once to float32; Qs = fp32(Q - qbar_g) on those rows (rows past N
+stay zero), quantised per block as above; the score gets the compensation
+back exactly, s = (sum_d q8 k8) sq sk scale + scale * (qbar_g . Ks_j), the
+dot product taken in float64 over the float32 operands, before the mask.
+Without quantisation error this is scale * Q . Ks, the same as without
+smoothing; with it, only the within-block deviation of Q is quantised.
+
 A second P V mode (``pv="bf16"`` or ``"f16"``) keeps the INT8 Q K^T steps and
 runs P V in 16 bits: V is used as given (the 16-bit input values, not
 quantised), P is rounded to the 16-bit type (round to nearest even) against
@@ -86,15 +96,38 @@ def quantise_fp8_channels(v_head):
     return v8, sv
 
 
-def quantise_head(q_head, k_head, v_head):
-    """All quantised operands of one (b, h) head."""
+def q_block_means(q_head, block=QBLOCK) -> np.ndarray:
+    """qbar [ceil(N/block), D]: the mean of each block's existing rows of Q,
+    summed in float64, divided by the row count, rounded once to float32."""
+    q = np.asarray(q_head, dtype=np.float64)
+    n, d = q.shape
+    nb = -(-n // block)
+    out = np.zeros((nb, d), dtype=np.float32)
+    for g in range(nb):
+        rows = q[g * block:min(n, (g + 1) * block)]
+        out[g] = (rows.sum(axis=0) / rows.shape[0]).astype(np.float32)
+    return out
+
+
+def quantise_head(q_head, k_head, v_head, smooth_q=False):
+    """All quantised operands of one (b, h) head; with smooth_q also the block
+    means of Q and the compensation qbar_g . Ks_j [blocks, N] (float64)."""
     km = k_mean(k_head)
     ks = (np.asarray(k_head, dtype=np.float32) - km[None, :]).astype(np.float32)
-    q8, sq = quantise_int8_blocks(q_head)
+    extra = {}
+    if smooth_q:
+        qf = np.asarray(q_head, dtype=np.float32)
+        qbar = q_block_means(qf)
+        rows_g = np.arange(qf.shape[0]) // QBLOCK
+        qs = (qf - qbar[rows_g]).astype(np.float32)
+        q8, sq = quantise_int8_blocks(qs)
+        extra = dict(qbar=qbar, comp=qbar.astype(np.float64) @ ks.astype(np.float64).T)
+    else:
+        q8, sq = quantise_int8_blocks(q_head)
     k8, sk = quantise_int8_blocks(ks)
     v8, sv = quantise_fp8_channels(v_head)
     return dict(kmean=km, ks=ks, q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv,
-                v16=np.asarray(v_head, dtype=np.float64))
+                v16=np.asarray(v_head, dtype=np.float64), **extra)
 
 
 def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quantise_p=True,
@@ -118,6 +151,8 @@ def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quanti
     s = s * qz["sq"][row_ids // QBLOCK].astype(np.float64)[:, None]
     s = s * qz["sk"][np.arange(n) // QBLOCK].astype(np.float64)[None, :]
     s = s * float(scale)
+    if "comp" in qz:                                        # Q smoothing: compensation back
+        s = s + float(scale) * qz["comp"][row_ids // QBLOCK]
     if mask is not None:
         s = s + np.broadcast_to(np.asarray(mask, dtype=np.float64), s.shape)
     if key_len is not None:
@@ -148,20 +183,21 @@ def _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len=None, quanti
 
 
 def emulate_rows(q_head, k_head, v_head, row_ids, scale, kv_block, key_len=None, qz=None,
-                 return_lse=False, pv="fp8", mask=None):
+                 return_lse=False, pv="fp8", mask=None, smooth_q=False):
     """Quantised-variant output for selected query rows of one head (float64, before
     the output rounding); with return_lse also the rows' log-sum-exp of the
     smoothed quantised scores.  mask: additive values for the selected rows,
-    broadcastable to [len(row_ids), N]."""
+    broadcastable to [len(row_ids), N].  smooth_q: Q smoothing with the
+    compensation (ignored when qz is given: qz says whether it holds one)."""
     if qz is None:
-        qz = quantise_head(q_head, k_head, v_head)
+        qz = quantise_head(q_head, k_head, v_head, smooth_q=smooth_q)
     return _quantised_attention_rows(row_ids, qz, scale, kv_block, key_len, return_lse=return_lse, pv=pv,
                                      mask=mask)
 
 
-def emulate(q, k, v, scale, kv_block, key_len=None, return_lse=False, pv="fp8", mask=None):
+def emulate(q, k, v, scale, kv_block, key_len=None, return_lse=False, pv="fp8", mask=None, smooth_q=False):
     """Full [B, H, N, D] emulation (small shapes); mask broadcastable to
-    [B, H, N, N] (additive)."""
+    [B, H, N, N] (additive); smooth_q: Q smoothing with compensation."""
     q = np.asarray(q)
     B, H, N, D = q.shape
     out = np.zeros((B, H, N, np.asarray(v).shape[3]))
@@ -172,5 +208,5 @@ def emulate(q, k, v, scale, kv_block, key_len=None, return_lse=False, pv="fp8", 
             kl = None if key_len is None else int(np.asarray(key_len)[b])
             out[b, h], lse[b, h] = emulate_rows(q[b, h], k[b, h], v[b, h], np.arange(N), scale, kv_block,
                                                 kl, return_lse=True, pv=pv,
-                                                mask=None if mfull is None else mfull[b, h])
+                                                mask=None if mfull is None else mfull[b, h], smooth_q=smooth_q)
     return (out, lse) if return_lse else out

@@ -305,3 +305,111 @@ def test_additive_mask_matches_key_length():
     a = sage.emulate_rows(q, k, v, np.arange(150), 0.25, 64, mask=mask)
     b = sage.emulate_rows(q, k, v, np.arange(150), 0.25, 64, key_len=97)
     assert np.array_equal(a, b)
+
+
+# ---- Q smoothing with compensation (handbook, section "SageAttention") ----
+
+def test_q_block_means_brute_force():
+    """Each 64-row block's mean over the rows that exist (the last block is
+    partial), by pure-Python loops in float64 rounded once to float32."""
+    rng = np.random.default_rng(21)
+    n, d = 150, 5
+    q = (rng.standard_normal((n, d)) * 3 + 1).astype(np.float32)
+    got = sage.q_block_means(q)
+    assert got.shape == (3, d) and got.dtype == np.float32
+    for g in range(3):
+        rows = range(64 * g, min(n, 64 * (g + 1)))
+        for c in range(d):
+            tot = 0.0
+            for r in rows:
+                tot += float(q[r, c])
+            assert got[g, c] == np.float32(tot / len(rows))
+
+
+def _lossless_smoothed_head(seed, d=8, n=256, step_q=2.0 ** -6, step_k=2.0 ** -5):
+    """A head where Q smoothing is lossless and plain Q quantisation is not.
+    Qs has codes in {-1,0,1} on channels 2-4 and +127 / -127 on channel 0 in
+    rows 0 / 32 of each block, mirrored about the block middle so every block
+    mean is zero; each block adds its own offset qbar_g (codes in {-1,0,1} on
+    channels 5-7, and 50 on channel 0, times step_q), so Q's block means are
+    exactly qbar_g and Q - qbar_g is exactly Qs, while Q itself reaches 177
+    steps in a block (plain INT8 Q is then lossy).  K as in the lossless head (channel 0 zero, mean
+    zero), so every score is an integer times step_q * step_k within 6 of 0."""
+    rng = np.random.default_rng(seed)
+    nb = n // 64
+    qs = np.zeros((n, d))
+    for g in range(nb):
+        half = rng.integers(-1, 2, (32, 3))
+        blk = np.zeros((64, d))
+        blk[:32, 2:5] = half
+        blk[32:, 2:5] = -half
+        blk[0, 0], blk[32, 0] = 127, -127
+        qs[64 * g:64 * (g + 1)] = blk
+    qbar = np.zeros((nb, d))
+    qbar[:, 5:8] = rng.integers(-1, 2, (nb, 3))
+    qbar[:, 5] = np.where(qbar[:, 5] == 0, 1, qbar[:, 5])     # every block offset nonzero
+    qbar[:, 0] = 50        # K's channel 0 is zero: no score change, but Q's block max becomes 177
+    q = (qs + np.repeat(qbar, 64, axis=0)) * step_q
+    _, k, v, _, _ = _lossless_head(seed + 1, d=d, n=n, step_q=step_q, step_k=step_k)
+    return q, k, v, qs * step_q, qbar * step_q, step_q, step_k
+
+
+@pytest.mark.parametrize("pv", ["fp8", "bf16"])
+def test_smoothing_lossless_equals_unquantised_formula(pv):
+    """The compensation restores qbar_g . Ks_j exactly: with lossless operands
+    the smoothed emulation equals unquantised attention (a dropped, mis-signed
+    or mis-indexed compensation would not), while plain quantisation of the
+    same Q is lossy."""
+    q, k, v, qs, qbar, step_q, step_k = _lossless_smoothed_head(31)
+    n = len(q)
+    qz = sage.quantise_head(q, k, v, smooth_q=True)
+    assert np.array_equal(qz["qbar"].astype(np.float64), qbar)
+    assert np.all(qz["sq"] == step_q) and np.array_equal(qz["q8"] * step_q, qs)
+    scale = math.log(2) / (step_q * step_k)
+    o_s, lse_s = sage.emulate_rows(q, k, v, np.arange(n), scale, 64, return_lse=True, pv=pv, smooth_q=True)
+    o_ref, lse_ref = attention.naive(q[None, None], k[None, None], v[None, None], scale)
+    assert np.abs(o_s - o_ref[0, 0]).max() <= 1e-12 * np.abs(v).max()
+    assert np.abs(lse_s - lse_ref[0, 0]).max() < 1e-9
+    o_plain = sage.emulate_rows(q, k, v, np.arange(n), scale, 64, pv=pv)
+    assert np.abs(o_plain - o_ref[0, 0]).max() > 1e-6
+
+
+def test_smoothing_helps_with_block_offsets():
+    """Queries with a large common offset per 64-token block: smoothing
+    quantises only the deviation, so the output (16-bit P V, leaving the Q K^T
+    quantisation as the main error) is closer to unquantised attention than
+    with plain INT8 Q; on offset-free queries it is no worse than a small
+    factor."""
+    rng = np.random.default_rng(41)
+    n, d = 320, 32
+    off = np.repeat(rng.choice([-20.0, 20.0], (n // 64, d)), 64, axis=0)
+    k, v = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    for q, must_gain in ((rng.standard_normal((n, d)) + off, True), (rng.standard_normal((n, d)), False)):
+        q = q.astype(np.float32)
+        ref, _ = attention.naive(q[None, None].astype(np.float64), k[None, None], v[None, None], d ** -0.5)
+        e = {}
+        for sm in (False, True):
+            o = sage.emulate_rows(q, k, v, np.arange(n), d ** -0.5, 64, smooth_q=sm, pv="bf16")
+            e[sm] = np.sqrt(((o - ref[0, 0]) ** 2).mean())
+        print("rms error plain / smoothed", e[False], e[True])
+        if must_gain:
+            assert e[True] < 0.5 * e[False]
+        else:
+            assert e[True] < 2.0 * e[False]
+
+
+def test_smoothing_partial_block_and_key_length():
+    """A partial last block takes the mean of its existing rows only, and
+    smoothing composes with a key-length mask and the 16-bit P V form."""
+    rng = np.random.default_rng(43)
+    n, d = 100, 16
+    q = (rng.standard_normal((n, d)) + 2.0).astype(np.float32)
+    k, v = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    qz = sage.quantise_head(q, k, v, smooth_q=True)
+    assert np.array_equal(qz["qbar"][1], sage.q_block_means(q[64:]).reshape(-1))
+    for pv in ("fp8", "f16"):
+        o = sage.emulate_rows(q, k, v, np.arange(n), 0.25, 64, key_len=70, pv=pv, smooth_q=True)
+        ref, _ = attention.naive(q[None, None].astype(np.float64), k[None, None], v[None, None], 0.25,
+                                 key_len=np.array([70]))
+        cos = (o * ref[0, 0]).sum() / np.linalg.norm(o) / np.linalg.norm(ref[0, 0])
+        assert cos > 0.999

@@ -26,6 +26,7 @@ FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_ARG, FA_ERR_HIP = -4, -5, -6, -7
 EXPORTED = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_fwd_ws_static", "fa_fwd_cross", "fa_fwd_strided",
             "fa_fwd_int8qk_workspace_bytes", "fa_fwd_int8qk",
             "fa_fwd_int8qk_pv16_workspace_bytes", "fa_fwd_int8qk_pv16",
+            "fa_fwd_int8qk_smooth_workspace_bytes", "fa_fwd_int8qk_smooth",
             "fa_merge", "fa_mfma_probe", "fa_cvt_probe", "fa_int8qk_kv_block", "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
 
@@ -89,6 +90,10 @@ def lib() -> ctypes.CDLL:
     h.fa_fwd_int8qk_pv16_workspace_bytes.restype = sz
     h.fa_fwd_int8qk_pv16.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     h.fa_fwd_int8qk_pv16.restype = i32
+    h.fa_fwd_int8qk_smooth_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    h.fa_fwd_int8qk_smooth_workspace_bytes.restype = sz
+    h.fa_fwd_int8qk_smooth.argtypes = [vp, vp, vp, vp, vp, mp, i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+    h.fa_fwd_int8qk_smooth.restype = i32
     h.fa_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     h.fa_merge.restype = i32
     h.fa_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
@@ -202,6 +207,16 @@ def mfma_peak(kind: int, ms_target: float = 40.0, device=None, warmup_ms: float 
         spent += run(iters)
     ts = sorted(run(iters) for _ in range(3))
     return wgs * 16 * iters * PROBE_FLOPS[kind] / (ts[1] * 1e-3) / 1e12
+
+
+def fa_fwd_int8qk_smooth_workspace_bytes(B, H, N, D, pv16) -> int:
+    return lib().fa_fwd_int8qk_smooth_workspace_bytes(B, H, N, D, pv16)
+
+
+def fa_fwd_int8qk_smooth(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, pv16, workspace,
+                         workspace_bytes, hip_stream) -> int:
+    return lib().fa_fwd_int8qk_smooth(q, k, v, o, lse, mask, B, H, N, D, scale, dtype, pv16, workspace,
+                                      workspace_bytes, hip_stream)
 
 
 def fa_int8qk_kv_block() -> int:
@@ -352,11 +367,13 @@ def fwd(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
 
 
 def fwd_int8qk(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] = None,
-               return_lse: bool = False, workspace=None, out=None, pv: str = "fp8"):
+               return_lse: bool = False, workspace=None, out=None, pv: str = "fp8", smooth_q: bool = False):
     """The INT8-QK variant for GPU tensors [B, H, N, 128] (bf16 / fp16): P V
     in FP8 (pv="fp8", fa_fwd_int8qk) or in the input's 16-bit type
     (pv="16", fa_fwd_int8qk_pv16).  Masks as for fwd (additive or boolean
-    attn_mask broadcastable to [B, H, N, N], or key_len [B])."""
+    attn_mask broadcastable to [B, H, N, N], or key_len [B]).  smooth_q:
+    Q smoothing with compensation as well (fa_fwd_int8qk_smooth; no
+    additive mask; its workspace holds a [B*H, N/64, N] float32 table)."""
     import torch
     if pv not in ("fp8", "16"):
         raise ValueError('pv must be "fp8" or "16"')
@@ -365,9 +382,15 @@ def fwd_int8qk(q, k, v, *, attn_mask=None, key_len=None, scale: Optional[float] 
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
-    size_fn, entry, where = ((fa_fwd_int8qk_workspace_bytes, fa_fwd_int8qk, "fa_fwd_int8qk") if pv == "fp8" else
-                             (fa_fwd_int8qk_pv16_workspace_bytes, fa_fwd_int8qk_pv16, "fa_fwd_int8qk_pv16"))
-    need = size_fn(B, H, N, D)
+    pv16 = 0 if pv == "fp8" else 1
+    if smooth_q:
+        need = fa_fwd_int8qk_smooth_workspace_bytes(B, H, N, D, pv16)
+        where = "fa_fwd_int8qk_smooth"
+        entry = lambda *a: fa_fwd_int8qk_smooth(*a[:12], pv16, *a[12:])  # noqa: E731
+    else:
+        size_fn, entry, where = ((fa_fwd_int8qk_workspace_bytes, fa_fwd_int8qk, "fa_fwd_int8qk") if pv == "fp8" else
+                                 (fa_fwd_int8qk_pv16_workspace_bytes, fa_fwd_int8qk_pv16, "fa_fwd_int8qk_pv16"))
+        need = size_fn(B, H, N, D)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
     keep = []
     m = _mask_struct(q, attn_mask, key_len, keep)

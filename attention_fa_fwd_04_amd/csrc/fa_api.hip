@@ -480,20 +480,26 @@ FA_API size_t fa_fwd_int8qk_pv16_workspace_bytes(int B, int H, int N, int D) {
   return fa::int8qk_workspace_layout(B, H, N, D, true).total;
 }
 
+FA_API size_t fa_fwd_int8qk_smooth_workspace_bytes(int B, int H, int N, int D, int pv16) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || (pv16 != 0 && pv16 != 1)) return 0;
+  return fa::int8qk_workspace_layout(B, H, N, D, pv16 != 0, true).total;
+}
+
 }  // extern "C"
 
 namespace {
-int int8qk_common(bool pv16, const void* q, const void* k, const void* v, void* o, float* lse,
+int int8qk_common(bool pv16, bool smooth, const void* q, const void* k, const void* v, void* o, float* lse,
                   const fa_mask_t* mask, int B, int H, int N, int D, float scale, fa_dtype_t dtype,
                   void* workspace, size_t workspace_bytes, void* hip_stream) {
-  const char* name = pv16 ? "fa_fwd_int8qk_pv16" : "fa_fwd_int8qk";
+  const char* name = smooth ? "fa_fwd_int8qk_smooth" : pv16 ? "fa_fwd_int8qk_pv16" : "fa_fwd_int8qk";
   int rc = check_common(q, k, v, o, lse, mask, B, H, N, D, scale);
   if (rc != FA_OK) return rc;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (D != 128) return FA_ERR_UNSUPPORTED;
   const int kind = mask ? mask->kind : FA_MASK_NONE;
+  if (smooth && kind == FA_MASK_ADDITIVE) return FA_ERR_UNSUPPORTED;
   if ((int64_t)(N + 256) * D * 2 > (int64_t)UINT32_MAX) return FA_ERR_SHAPE;
-  const fa::Int8Layout lay = fa::int8qk_workspace_layout(B, H, N, D, pv16);
+  const fa::Int8Layout lay = fa::int8qk_workspace_layout(B, H, N, D, pv16, smooth);
   if (!workspace) return FA_ERR_WORKSPACE;
   if (workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
@@ -505,14 +511,14 @@ int int8qk_common(bool pv16, const void* q, const void* k, const void* v, void* 
                  name, dtype_name(dtype), D, kind, B, H, N, lay.total);
   if (pv16) {
     if (dtype == FA_BF16)
-      rc = fa::launch_int8qk_pv16<__bf16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, st);
+      rc = fa::launch_int8qk_pv16<__bf16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, smooth, st);
     else
-      rc = fa::launch_int8qk_pv16<_Float16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, st);
+      rc = fa::launch_int8qk_pv16<_Float16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, smooth, st);
   } else {
     if (dtype == FA_BF16)
-      rc = fa::launch_int8qk<__bf16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, st);
+      rc = fa::launch_int8qk<__bf16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, smooth, st);
     else
-      rc = fa::launch_int8qk<_Float16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, st);
+      rc = fa::launch_int8qk<_Float16>(q, k, v, o, lse, kind, m, B, H, N, scale, workspace, lay, smooth, st);
   }
   if (rc != FA_OK) return rc;
   return record_launch(name);
@@ -525,7 +531,7 @@ FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, f
                   const fa_mask_t* mask, int B, int H, int N, int D, float scale,
                   fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                   void* hip_stream) {
-  return int8qk_common(false, q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace, workspace_bytes,
+  return int8qk_common(false, false, q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace, workspace_bytes,
                        hip_stream);
 }
 
@@ -533,8 +539,17 @@ FA_API int fa_fwd_int8qk_pv16(const void* q, const void* k, const void* v, void*
                               const fa_mask_t* mask, int B, int H, int N, int D, float scale,
                               fa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                               void* hip_stream) {
-  return int8qk_common(true, q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace, workspace_bytes,
+  return int8qk_common(true, false, q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace, workspace_bytes,
                        hip_stream);
+}
+
+FA_API int fa_fwd_int8qk_smooth(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                                fa_dtype_t dtype, int pv16, void* workspace, size_t workspace_bytes,
+                                void* hip_stream) {
+  if (pv16 != 0 && pv16 != 1) return FA_ERR_ARG;
+  return int8qk_common(pv16 != 0, true, q, k, v, o, lse, mask, B, H, N, D, scale, dtype, workspace,
+                       workspace_bytes, hip_stream);
 }
 
 FA_API int fa_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
@@ -638,6 +653,6 @@ FA_API const char* fa_status_string(int status) {
 
 FA_API const char* fa_last_hip_error(void) { return g_hip_err; }
 
-FA_API int fa_abi_version(void) { return 3; }
+FA_API int fa_abi_version(void) { return 4; }
 
 }  // extern "C"

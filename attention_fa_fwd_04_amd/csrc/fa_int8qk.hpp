@@ -17,6 +17,12 @@
 //                   (no lazy rescale: P <= 1 is what makes the x448 FP8 scale
 //                   valid), rounded to e4m3 as 448 P; l sums the unrounded
 //                   448 P; O = acc * sv / l.
+// With Q smoothing (the same section's "Q and K minus their block means")
+// the Q slice of int8_quant also takes each 64-token block's mean qbar
+// (float64 sum over the block's rows, rounded once to float32) and quantises
+// Q - qbar; one more launch, int8_comp, tabulates the compensation
+// scale log2(e) qbar_g . (K_j - kmean) in float64, rounded to float32, per
+// (b,h, block, key); the main loop adds the wave's block row to its scores.
 #pragma once
 
 #include "fa_common.hpp"
@@ -38,11 +44,13 @@ struct Int8Layout {
   int splits;        // token splits of the K-sum / V-absmax reduction
   int split_rows;    // tokens per split
   size_t q8, k8, v8t, sq, sk, sv, vmul, kmean, kpart, vpart;
+  size_t qbar, comp;   // Q smoothing only (0 otherwise)
   size_t total;
 };
 
 // pv16: the INT8-QK / 16-bit-PV form keeps V^T in the input's 16-bit type.
-inline Int8Layout int8qk_workspace_layout(int B, int H, int N, int D, bool pv16 = false) {
+// smooth: Q smoothing adds the block means and the compensation table.
+inline Int8Layout int8qk_workspace_layout(int B, int H, int N, int D, bool pv16 = false, bool smooth = false) {
   Int8Layout L{};
   const size_t bh = (size_t)B * H;
   L.npad = (N + kQBlock - 1) / kQBlock * kQBlock;
@@ -62,6 +70,10 @@ inline Int8Layout int8qk_workspace_layout(int B, int H, int N, int D, bool pv16 
   L.kmean = take(bh * (size_t)D * 4);              // f32 [BH, D]
   L.kpart = take(bh * (size_t)L.splits * D * 8);   // f64 [BH, splits, D]
   L.vpart = take(bh * (size_t)L.splits * D * 4);   // f32 [BH, splits, D]
+  if (smooth) {
+    L.qbar = take(bh * L.groups * (size_t)D * 4);  // f32 [BH, groups, D]
+    L.comp = take(bh * L.groups * (size_t)L.npad * 4);   // f32 [BH, groups, npad], log2 units
+  }
   L.total = off;
   return L;
 }
@@ -138,11 +150,15 @@ __global__ __launch_bounds__(128) void int8_finalize_kernel(
 }
 
 // One 64-token block of Q (isk == 0) or K - kmean (isk == 1), 256 threads.
+// qbar != nullptr (Q only): Q smoothing.  The block's mean over its rows
+// below N is summed in float64 (thread partials over its 4 rows, then 16
+// partials per channel through LDS: 16 KB of dsum), rounded once to float32,
+// stored, and subtracted (in float32) from those rows before quantising.
 template <typename T, int D>
 __device__ __forceinline__ void quant_qk_block(
     const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ kmean,
     int8_t* __restrict__ q8, int8_t* __restrict__ k8, float* __restrict__ sq, float* __restrict__ sk,
-    int N, int npad, int groups, int g, int bh, int isk, float* wmax) {
+    float* __restrict__ qbar, int N, int npad, int groups, int g, int bh, int isk, float* wmax, double* dsum) {
   static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
   constexpr int CH = D / 8;
   const T* X = (isk ? K : Q) + (size_t)bh * N * D;
@@ -165,12 +181,43 @@ __device__ __forceinline__ void quant_qk_block(
       km[4] = hi.x; km[5] = hi.y; km[6] = hi.z; km[7] = hi.w;
     }
 #pragma unroll
+    for (int e = 0; e < 8; ++e) x[i][e] = (float)v[e] - km[e];
+  }
+  if (!isk && qbar != nullptr) {
+    // this thread's rows t / 16 + 16 i, channels 8 (t % 16) + e
+    const int c = t % CH;
+#pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float f = (float)v[e] - km[e];
-      x[i][e] = f;
-      a = fmaxf(a, fabsf(f));
+      double p = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p += (double)x[i][e];         // rows past N hold 0
+      dsum[t * 8 + e] = p;
+    }
+    __syncthreads();
+    float* qb = wmax + 4;                     // 128 floats after the 4 wave maxima
+    if (t < D) {
+      const int cc = t / 8, e = t % 8;
+      double tot = 0.0;
+      for (int j = 0; j < 256 / CH; ++j) tot += dsum[(cc + CH * j) * 8 + e];
+      const int rows = min(kQBlock, N - g * kQBlock);
+      const float mean = (float)(tot / (double)rows);
+      qb[t] = mean;
+      qbar[((size_t)bh * groups + g) * D + t] = mean;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = g * kQBlock + (t + 256 * i) / CH;
+      if (row < N) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] - qb[c * 8 + e];
+      }
     }
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[i][e]));
   for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
   if ((t & 63) == 0) wmax[t >> 6] = a;
   __syncthreads();
@@ -281,20 +328,88 @@ __device__ __forceinline__ void v16t_block(const T* __restrict__ V, T* __restric
 // The quantisation launch: blockIdx = (64-token block, b * H + h, which):
 // which 0 quantises Q, 1 K - kmean (per-block INT8 codes and scales), 2 V
 // (e4m3 V^T, or the 16-bit V^T of the INT8-QK / 16-bit-PV form).
-template <typename T, int D, bool PV16>
+template <typename T, int D, bool PV16, bool SMOOTH>
 __global__ __launch_bounds__(256) void int8_quant_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ kmean,
     const float* __restrict__ vmul, int8_t* __restrict__ q8, int8_t* __restrict__ k8, void* __restrict__ vt,
-    float* __restrict__ sq, float* __restrict__ sk, int N, int npad, int groups) {
+    float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ qbar, int N, int npad, int groups) {
   constexpr int VT_BYTES = PV16 ? D * (64 + 8) * 2 : D * (kQBlock + 8);
-  __shared__ __attribute__((aligned(16))) uint8_t lds[VT_BYTES];
+  constexpr int SM_BYTES = 256 * 8 * 8 + 1024;   // float64 partials + wave maxima and block means
+  constexpr int BYTES = (SMOOTH && SM_BYTES > VT_BYTES) ? SM_BYTES : VT_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[BYTES];
   const int g = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
   if (which < 2) {
-    quant_qk_block<T, D>(Q, K, kmean, q8, k8, sq, sk, N, npad, groups, g, bh, which, reinterpret_cast<float*>(lds));
+    quant_qk_block<T, D>(Q, K, kmean, q8, k8, sq, sk, SMOOTH ? qbar : nullptr, N, npad, groups, g, bh, which,
+                         reinterpret_cast<float*>(lds + (SMOOTH ? 256 * 8 * 8 : 0)), reinterpret_cast<double*>(lds));
   } else if constexpr (PV16) {
     v16t_block<T, D>(V, static_cast<T*>(vt), N, npad, g, bh, reinterpret_cast<T*>(lds));
   } else {
     quant_v_block<T, D>(V, vmul, static_cast<uint8_t*>(vt), N, npad, g, bh, lds);
+  }
+}
+
+// Q smoothing's compensation table, tile of 64 blocks x 64 keys per
+// workgroup of 256 threads: comp[bh][g][j] = fp32(c2 * sum_d qbar[g][d] *
+// Ks[j][d]) with Ks = fp32(K - kmean) (keys past N give 0) and c2 = scale *
+// log2(e), the products and sums in float64.  Each thread owns 4 blocks x 4
+// keys; LDS rows of 129 floats keep the 16 keys and the 4 blocks a wave
+// reads per channel on distinct banks.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void int8_comp_kernel(
+    const T* __restrict__ K, const float* __restrict__ kmean, const float* __restrict__ qbar,
+    float* __restrict__ comp, int N, int npad, int groups, double c2) {
+  static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
+  constexpr int RS = D + 1;
+  __shared__ float qs[64 * RS];
+  __shared__ float ks[64 * RS];
+  const int j0 = blockIdx.x * 64, g0 = blockIdx.y * 64, bh = blockIdx.z, t = threadIdx.x;
+  const T* Kh = K + (size_t)bh * N * D;
+  const float* km = kmean + (size_t)bh * D;
+  // stage: 64 rows x 16 chunks of 8 channels each, for K and for qbar
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int it = t + 256 * i, r = it / 16, c = it % 16;
+    float kv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (j0 + r < N) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(Kh + (size_t)(j0 + r) * D + 8 * c);
+      const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kv[e] = (float)v[e] - km[8 * c + e];
+    }
+    float qv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (g0 + r < groups) {
+      const float* src = qbar + ((size_t)bh * groups + g0 + r) * D + 8 * c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = src[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ks[r * RS + 8 * c + e] = kv[e];
+      qs[r * RS + 8 * c + e] = qv[e];
+    }
+  }
+  __syncthreads();
+  const int tg = t / 16, tj = t % 16;
+  double acc[4][4] = {};
+  for (int d = 0; d < D; ++d) {
+    double qd[4], kd[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) qd[a] = (double)qs[(4 * tg + a) * RS + d];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) kd[b] = (double)ks[(4 * tj + b) * RS + d];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fma(qd[a], kd[b], acc[a][b]);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int g = g0 + 4 * tg + a;
+    if (g < groups) {
+      const f32x4 w = {(float)(acc[a][0] * c2), (float)(acc[a][1] * c2), (float)(acc[a][2] * c2),
+                       (float)(acc[a][3] * c2)};
+      *reinterpret_cast<f32x4*>(comp + ((size_t)bh * groups + g) * npad + j0 + 4 * tj) = w;
+    }
   }
 }
 
@@ -318,11 +433,14 @@ __device__ __forceinline__ float unbias(int a) { return __builtin_bit_cast(float
 // LDS by buffer-load DMA into unpadded, chunk-swizzled rows (no staging
 // registers or LDS stores; the operand reads are conflict-free).
 
-template <typename T, int MASK>
+// SQ: Q smoothing; comp holds the compensation table (log2 units), whose
+// row for the wave's query block is added to every score (MASK is then
+// none or a key length).
+template <typename T, int MASK, bool SQ>
 __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
     const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
-    MaskArgs mask, T* __restrict__ O, float* __restrict__ LSE,
+    const float* __restrict__ comp, MaskArgs mask, T* __restrict__ O, float* __restrict__ LSE,
     int H, int N, int npad, int groups, int nqt, float c_log2) {
   constexpr int D = 128, BC = kInt8Bc, BR = 128, NT = 256;
   constexpr int KSTR = D;                       // int8 K row (128 bytes, chunks swizzled)
@@ -365,6 +483,12 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh + (int64_t)(q_ok ? q_row : 0) * mask.sq;
     mvec = mask_rows_vec4(mask);
   }
+  static_assert(!(SQ && MASK == kMaskAdd), "Q smoothing takes no additive mask");
+  if constexpr (SQ) {   // the compensation row of the wave's query block (rows are npad floats, aligned)
+    mrow = comp + ((size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)) * npad;
+    mvec = true;
+  }
+  constexpr bool kRowTerm = SQ || MASK == kMaskAdd;   // a per-key term on every tile
 
   // Tiles reach LDS by buffer-load DMA (1 KB per instruction, two K and two
   // V instructions per wave and tile).  Rows are unpadded; the lane landing
@@ -407,7 +531,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     // additive mask values of this lane's 32 keys (keys past N read -inf),
     // loaded ahead of the MFMAs (measured no faster issued before the DMA)
     float mk[32];
-    if constexpr (MASK == kMaskAdd) load_mask_tile<2>(mk, mrow, mask.sk, mvec, j * BC, N, lh);
+    if constexpr (kRowTerm) load_mask_tile<2>(mk, mrow, SQ ? 1 : mask.sk, mvec, j * BC, n_eff, lh);
     const uint8_t* kb = smem + buf * BUF;
     const uint8_t* vb = kb + KBYTES;
     const int kv0 = j * BC;
@@ -438,7 +562,9 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if constexpr (MASK == kMaskAdd)
+          if constexpr (SQ)                           // table already in log2 units; -inf past n_eff
+            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i]);
+          else if constexpr (MASK == kMaskAdd)
             s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i] * kLog2e);
           else
             s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
@@ -505,7 +631,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   dma_tile(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  if constexpr (MASK == kMaskAdd) {
+  if constexpr (kRowTerm) {
     for (int j = 0; j < ntiles; ++j) step(j, BoolTag<true>{});
   } else {
     const int nfull = n_eff / BC;
@@ -538,10 +664,10 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
 // the running max) and V^T read unquantised from the workspace (keys permuted
 // per 32 by v16_pos); P V runs on the 16-bit 32x32x16 MFMA, four per 32
 // channels per 64-key tile.
-template <typename T, int MASK>
+template <typename T, int MASK, bool SQ>
 __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const T* __restrict__ vt,
-    const float* __restrict__ sq, const float* __restrict__ sk,
+    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ comp,
     MaskArgs mask, T* __restrict__ O, float* __restrict__ LSE,
     int H, int N, int npad, int groups, int nqt, float c_log2) {
   constexpr int D = 128, BC = kInt8Bc, BR = 128, NT = 256;
@@ -585,6 +711,12 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
     mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh + (int64_t)(q_ok ? q_row : 0) * mask.sq;
     mvec = mask_rows_vec4(mask);
   }
+  static_assert(!(SQ && MASK == kMaskAdd), "Q smoothing takes no additive mask");
+  if constexpr (SQ) {   // the compensation row of the wave's query block (rows are npad floats, aligned)
+    mrow = comp + ((size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)) * npad;
+    mvec = true;
+  }
+  constexpr bool kRowTerm = SQ || MASK == kMaskAdd;   // a per-key term on every tile
 
   // staging: K tile 64 rows x 8 chunks (2 per thread), V^T tile 128 rows x 8
   // chunks (4 per thread)
@@ -628,7 +760,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
     // issued before the next tile's loads so that waiting for them does not
     // wait for those too (loads complete in issue order)
     float mk[32];
-    if constexpr (MASK == kMaskAdd) load_mask_tile<2>(mk, mrow, mask.sk, mvec, j * BC, N, lh);
+    if constexpr (kRowTerm) load_mask_tile<2>(mk, mrow, SQ ? 1 : mask.sk, mvec, j * BC, n_eff, lh);
     load_tile(j + 1);
     const uint8_t* kb = smem + buf * BUF;
     const uint8_t* vb = kb + KBYTES;
@@ -659,7 +791,9 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if constexpr (MASK == kMaskAdd)
+          if constexpr (SQ)                           // table already in log2 units; -inf past n_eff
+            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i]);
+          else if constexpr (MASK == kMaskAdd)
             s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i] * kLog2e);
           else
             s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
@@ -724,7 +858,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
   load_tile(0);
   store_tile(0);
   __syncthreads();
-  if constexpr (MASK == kMaskAdd) {
+  if constexpr (kRowTerm) {
     for (int j = 0; j < ntiles; ++j) step(j, BoolTag<true>{});
   } else {
     const int nfull = n_eff / BC;
@@ -749,75 +883,84 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
   }
 }
 
-template <typename T>
-int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse, int mask_kind, MaskArgs m,
-                       int B, int H, int N, float scale, void* workspace, const Int8Layout& L, hipStream_t st) {
+// Prepass launches (statistics, quantisation, and with Q smoothing the
+// compensation table) shared by both P V forms; returns the operands.
+struct Int8Ops {
+  int8_t *q8, *k8;
+  void* vt;
+  float *sq, *sk, *sv, *comp;
+};
+
+template <typename T, bool PV16>
+Int8Ops int8_prepass(const void* q, const void* k, const void* v, int B, int H, int N, float scale, void* workspace,
+                     const Int8Layout& L, bool smooth, hipStream_t st) {
   constexpr int D = 128;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  int8_t* q8 = reinterpret_cast<int8_t*>(ws + L.q8);
-  int8_t* k8 = reinterpret_cast<int8_t*>(ws + L.k8);
-  T* vt = reinterpret_cast<T*>(ws + L.v8t);
-  float* sq = reinterpret_cast<float*>(ws + L.sq);
-  float* sk = reinterpret_cast<float*>(ws + L.sk);
-  float* sv = reinterpret_cast<float*>(ws + L.sv);
+  Int8Ops op{reinterpret_cast<int8_t*>(ws + L.q8), reinterpret_cast<int8_t*>(ws + L.k8), ws + L.v8t,
+             reinterpret_cast<float*>(ws + L.sq), reinterpret_cast<float*>(ws + L.sk),
+             reinterpret_cast<float*>(ws + L.sv), smooth ? reinterpret_cast<float*>(ws + L.comp) : nullptr};
   float* vmul = reinterpret_cast<float*>(ws + L.vmul);
   float* kmean = reinterpret_cast<float*>(ws + L.kmean);
   double* kpart = reinterpret_cast<double*>(ws + L.kpart);
   float* vpart = reinterpret_cast<float*>(ws + L.vpart);
+  float* qbar = smooth ? reinterpret_cast<float*>(ws + L.qbar) : nullptr;
   const T* Q = static_cast<const T*>(q);
   const T* K = static_cast<const T*>(k);
   const T* V = static_cast<const T*>(v);
   const int BH = B * H;
   hipLaunchKernelGGL((int8_stats_kernel<T, D>), dim3(L.splits, BH), dim3(256), 0, st, K, V, kpart, vpart, N, L.splits,
                      L.split_rows);
-  hipLaunchKernelGGL((int8_finalize_kernel<D>), dim3(BH), dim3(D), 0, st, kpart, vpart, kmean, sv, vmul, N, L.splits);
-  hipLaunchKernelGGL((int8_quant_kernel<T, D, true>), dim3(L.groups, BH, 3), dim3(256), 0, st, Q, K, V, kmean, vmul, q8,
-                     k8, static_cast<void*>(vt), sq, sk, N, L.npad, L.groups);
+  hipLaunchKernelGGL((int8_finalize_kernel<D>), dim3(BH), dim3(D), 0, st, kpart, vpart, kmean, op.sv, vmul, N, L.splits);
+  if (smooth) {
+    hipLaunchKernelGGL((int8_quant_kernel<T, D, PV16, true>), dim3(L.groups, BH, 3), dim3(256), 0, st, Q, K, V, kmean,
+                       vmul, op.q8, op.k8, op.vt, op.sq, op.sk, qbar, N, L.npad, L.groups);
+    hipLaunchKernelGGL((int8_comp_kernel<T, D>), dim3(L.npad / 64, (L.groups + 63) / 64, BH), dim3(256), 0, st, K,
+                       kmean, qbar, op.comp, N, L.npad, L.groups, (double)scale * 1.4426950408889634);
+  } else {
+    hipLaunchKernelGGL((int8_quant_kernel<T, D, PV16, false>), dim3(L.groups, BH, 3), dim3(256), 0, st, Q, K, V, kmean,
+                       vmul, op.q8, op.k8, op.vt, op.sq, op.sk, nullptr, N, L.npad, L.groups);
+  }
+  return op;
+}
+
+template <typename T>
+int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse, int mask_kind, MaskArgs m,
+                       int B, int H, int N, float scale, void* workspace, const Int8Layout& L, bool smooth,
+                       hipStream_t st) {
+  const Int8Ops op = int8_prepass<T, true>(q, k, v, B, H, N, scale, workspace, L, smooth, st);
   const int nqt = (N + 127) / 128;
-  const int grid = BH * nqt;
+  const int grid = B * H * nqt;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, q8, k8, vt, sq, sk, m, static_cast<T*>(o), lse, H, N,
-                       L.npad, L.groups, nqt, scale * kLog2e);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, op.q8, op.k8, static_cast<const T*>(op.vt), op.sq, op.sk,
+                       op.comp, m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
   };
-  if (mask_kind == kMaskLen) go(fa_int8qk_pv16_kernel<T, kMaskLen>);
-  else if (mask_kind == kMaskAdd) go(fa_int8qk_pv16_kernel<T, kMaskAdd>);
-  else go(fa_int8qk_pv16_kernel<T, kMaskNone>);
+  if (smooth) {
+    if (mask_kind == kMaskLen) go(fa_int8qk_pv16_kernel<T, kMaskLen, true>);
+    else go(fa_int8qk_pv16_kernel<T, kMaskNone, true>);
+  } else if (mask_kind == kMaskLen) go(fa_int8qk_pv16_kernel<T, kMaskLen, false>);
+  else if (mask_kind == kMaskAdd) go(fa_int8qk_pv16_kernel<T, kMaskAdd, false>);
+  else go(fa_int8qk_pv16_kernel<T, kMaskNone, false>);
   return FA_OK;
 }
 
 template <typename T>
 int launch_int8qk(const void* q, const void* k, const void* v, void* o, float* lse, int mask_kind, MaskArgs m,
-                  int B, int H, int N, float scale, void* workspace, const Int8Layout& L, hipStream_t st) {
-  constexpr int D = 128;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  int8_t* q8 = reinterpret_cast<int8_t*>(ws + L.q8);
-  int8_t* k8 = reinterpret_cast<int8_t*>(ws + L.k8);
-  uint8_t* v8t = ws + L.v8t;
-  float* sq = reinterpret_cast<float*>(ws + L.sq);
-  float* sk = reinterpret_cast<float*>(ws + L.sk);
-  float* sv = reinterpret_cast<float*>(ws + L.sv);
-  float* vmul = reinterpret_cast<float*>(ws + L.vmul);
-  float* kmean = reinterpret_cast<float*>(ws + L.kmean);
-  double* kpart = reinterpret_cast<double*>(ws + L.kpart);
-  float* vpart = reinterpret_cast<float*>(ws + L.vpart);
-  const T* Q = static_cast<const T*>(q);
-  const T* K = static_cast<const T*>(k);
-  const T* V = static_cast<const T*>(v);
-  const int BH = B * H;
-  hipLaunchKernelGGL((int8_stats_kernel<T, D>), dim3(L.splits, BH), dim3(256), 0, st, K, V, kpart, vpart, N, L.splits,
-                     L.split_rows);
-  hipLaunchKernelGGL((int8_finalize_kernel<D>), dim3(BH), dim3(D), 0, st, kpart, vpart, kmean, sv, vmul, N, L.splits);
-  hipLaunchKernelGGL((int8_quant_kernel<T, D, false>), dim3(L.groups, BH, 3), dim3(256), 0, st, Q, K, V, kmean, vmul,
-                     q8, k8, static_cast<void*>(v8t), sq, sk, N, L.npad, L.groups);
+                  int B, int H, int N, float scale, void* workspace, const Int8Layout& L, bool smooth,
+                  hipStream_t st) {
+  const Int8Ops op = int8_prepass<T, false>(q, k, v, B, H, N, scale, workspace, L, smooth, st);
   const int nqt = (N + 127) / 128;
-  const int grid = BH * nqt;
+  const int grid = B * H * nqt;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, q8, k8, v8t, sq, sk, sv, m, static_cast<T*>(o), lse, H, N,
-                       L.npad, L.groups, nqt, scale * kLog2e);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, op.q8, op.k8, static_cast<const uint8_t*>(op.vt), op.sq,
+                       op.sk, op.sv, op.comp, m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt,
+                       scale * kLog2e);
   };
-  if (mask_kind == kMaskLen) go(fa_int8qk_kernel<T, kMaskLen>);
-  else if (mask_kind == kMaskAdd) go(fa_int8qk_kernel<T, kMaskAdd>);
-  else go(fa_int8qk_kernel<T, kMaskNone>);
+  if (smooth) {
+    if (mask_kind == kMaskLen) go(fa_int8qk_kernel<T, kMaskLen, true>);
+    else go(fa_int8qk_kernel<T, kMaskNone, true>);
+  } else if (mask_kind == kMaskLen) go(fa_int8qk_kernel<T, kMaskLen, false>);
+  else if (mask_kind == kMaskAdd) go(fa_int8qk_kernel<T, kMaskAdd, false>);
+  else go(fa_int8qk_kernel<T, kMaskNone, false>);
   return FA_OK;
 }
 

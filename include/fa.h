@@ -247,6 +247,38 @@ FA_API int fa_fwd_int8qk_pv16(const void* q, const void* k, const void* v, void*
                               void* hip_stream);
 
 /*
+ * The same method with Q smoothing as well (handbook page, section
+ * "SageAttention": Q and K minus their block means).  pv16 = 0 runs the P V
+ * of fa_fwd_int8qk (FP8), pv16 = 1 that of fa_fwd_int8qk_pv16 (16-bit).
+ * Step 2 quantises Q - qbar_g instead of Q, where qbar_g is the mean of the
+ * rows of 64-token block g that exist (rows < N), summed in float64 and
+ * rounded once to float32 (the subtraction in float32, rows >= N stay 0);
+ * step 4 adds the compensation back to every score:
+ *     S = (Q8 . K8) * sq * sk * scale + scale * (qbar_g . (K_j - kmean))
+ * the dot product in float64 over the float32 operands, tabulated per
+ * (b, h, block, key) and rounded once to float32 (in log2 units, times
+ * log2 e) — without quantisation error this is scale * Q . (K - kmean), as
+ * without smoothing; with it, only each block's deviation from its mean is
+ * quantised, which helps when query blocks share a large common offset.
+ * lse as for fa_fwd_int8qk.  Masks: NONE or KEYLEN (ADDITIVE gives
+ * FA_ERR_UNSUPPORTED); FA_ERR_ARG for pv16 outside {0, 1}; otherwise the
+ * arguments and errors of fa_fwd_int8qk.
+ *   workspace  at least fa_fwd_int8qk_smooth_workspace_bytes(B,H,N,D,pv16)
+ *              bytes, 256-byte aligned: the regions of the chosen form's
+ *              workspace, then
+ *                qbar  f32  [BH, Np/64, D]   block means of Q
+ *                comp  f32  [BH, Np/64, Np]  scale * log2(e) * qbar . (K - kmean)
+ *              (B*H*N*N/16 bytes for the table: 14.5 GB at B=1, H=40,
+ *              N=76112).  fa_fwd_int8qk_smooth_workspace_bytes returns 0 for
+ *              non-positive sizes or pv16 outside {0, 1}.
+ */
+FA_API size_t fa_fwd_int8qk_smooth_workspace_bytes(int B, int H, int N, int D, int pv16);
+FA_API int fa_fwd_int8qk_smooth(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const fa_mask_t* mask, int B, int H, int N, int D, float scale,
+                                fa_dtype_t dtype, int pv16, void* workspace, size_t workspace_bytes,
+                                void* hip_stream);
+
+/*
  * Merge two attention results computed for the same queries over disjoint
  * key sets (K/V split along the sequence, as in ring attention: essay page,
  * section 6.2):

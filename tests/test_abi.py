@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_static_queries(lib):
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
     assert fa.fa_int8qk_kv_block() % 64 == 0
     assert fa.fa_status_string(0) == "ok"
     for code in range(-7, 0):
@@ -234,3 +234,32 @@ def test_fwd_ws_static_outside_split_domain(lib):
     assert call(scale=0.0) == fa.FA_ERR_ARG
     assert call(B=0) == fa.FA_ERR_SHAPE
     assert call(q=P + 8) == fa.FA_ERR_ALIGN
+
+
+def test_int8qk_smooth_validation(lib):
+    """Q smoothing's entry point: the workspace adds the block means and the
+    [B*H, Np/64, Np] float32 compensation table to the chosen P V form's."""
+    for pv16, base in ((0, fa.fa_fwd_int8qk_workspace_bytes), (1, fa.fa_fwd_int8qk_pv16_workspace_bytes)):
+        ws = fa.fa_fwd_int8qk_smooth_workspace_bytes(1, 2, 1000, 128, pv16)
+        groups, npad = 16, 1024
+        assert ws >= base(1, 2, 1000, 128) + 2 * groups * 128 * 4 + 2 * groups * npad * 4
+        assert ws <= base(1, 2, 1000, 128) + 2 * groups * 128 * 4 + 2 * groups * npad * 4 + 512
+    assert fa.fa_fwd_int8qk_smooth_workspace_bytes(1, 2, 1000, 128, 2) == 0
+    assert fa.fa_fwd_int8qk_smooth_workspace_bytes(0, 2, 1000, 128, 0) == 0
+    ws = fa.fa_fwd_int8qk_smooth_workspace_bytes(1, 2, 1000, 128, 0)
+
+    def call(**kw):
+        a = dict(dtype=fa.FA_BF16, D=128, ws=P, wsb=ws, mask=None, N=1000, pv16=0)
+        a.update(kw)
+        return fa.fa_fwd_int8qk_smooth(P, P, P, P, None, a["mask"], 1, 2, a["N"], a["D"], 0.1, a["dtype"],
+                                       a["pv16"], a["ws"], a["wsb"], None)
+    assert call(pv16=2) == fa.FA_ERR_ARG
+    assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert call(D=40) == fa.FA_ERR_UNSUPPORTED
+    add = fa.fa_mask_t(fa.FA_MASK_ADDITIVE, P, 0, 0, 0, 1)
+    assert call(mask=ctypes.byref(add)) == fa.FA_ERR_UNSUPPORTED
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=fa.fa_fwd_int8qk_workspace_bytes(1, 2, 1000, 128)) == fa.FA_ERR_WORKSPACE
+    assert call(pv16=1) == fa.FA_ERR_WORKSPACE          # the 16-bit form's workspace is larger
+    assert call(ws=P + 16) == fa.FA_ERR_ALIGN
+    assert call(N=1 << 24) == fa.FA_ERR_SHAPE

@@ -22,6 +22,7 @@ relative RMS error sits within about 20 % of the rounding noise (ROW_MEDIAN),
 at most 1 % of rows exceed five times that, and the relative RMS error over
 the whole case and the cosine leave room for the flips (REL_RMS, COS_EMU).
 """
+import math
 import sys
 
 import numpy as np
@@ -406,3 +407,130 @@ def test_additive_mask_layouts_int8(dev, pv):
         assert np.array_equal(np.isneginf(lg), np.isneginf(ref_lse))
         fin = np.isfinite(ref_lse)
         assert np.abs(lg[fin] - ref_lse[fin]).max() < 1e-4
+
+
+# ---- Q smoothing (fa_fwd_int8qk_smooth) ----
+
+def offset_queries(inp, amp, seed):
+    """Q plus a common offset per (b, h, 64-token block, channel) of +-amp, in
+    Q's own dtype: the structure Q smoothing is for."""
+    q = inp["q"]
+    B, H, N, D = q.shape
+    g = torch.Generator().manual_seed(seed)
+    nb = (N + 63) // 64
+    off = (torch.randint(0, 2, (B, H, nb, D), generator=g).float() * 2 - 1) * amp
+    off = off.repeat_interleave(64, dim=2)[:, :, :N]
+    out = dict(inp)
+    out["q"] = (q.float() + off).to(q.dtype)
+    return out
+
+
+@pytest.mark.parametrize("pv", ["fp8", "16"])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_smooth_operands_bit_exact(dev, dt, pv):
+    """The smoothed Q codes and scales and the block means bit-exact against
+    the oracle; the compensation table within float32 rounding of the
+    oracle's float64 value times scale * log2(e)."""
+    w = WORKLOADS[5].with_shape(H=2, N=200, dtype=dt)
+    inp = offset_queries(make_inputs(w), 4.0, 1)
+    B, H, N, D = w.B, w.H, w.N, w.D
+    pv16 = 0 if pv == "fp8" else 1
+    ws = torch.empty(fa.fa_fwd_int8qk_smooth_workspace_bytes(B, H, N, D, pv16), dtype=torch.uint8, device=dev)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    fa.fwd_int8qk(q, k, v, workspace=ws, pv=pv, smooth_q=True)
+    torch.cuda.synchronize()
+    buf = ws.cpu().numpy()
+    lay, npad = layout(B, H, N, D, 1 if pv == "fp8" else 2)
+    g = npad // 64
+    base = (fa.fa_fwd_int8qk_workspace_bytes if pv == "fp8" else fa.fa_fwd_int8qk_pv16_workspace_bytes)(B, H, N, D)
+    qbar_off = base
+    comp_off = _a256(qbar_off + B * H * g * D * 4)
+
+    def region(off, nbytes, dtype, shape):
+        return buf[off:off + nbytes].view(dtype).reshape(shape)
+
+    q8 = region(*lay["q8"], np.int8, (B * H, npad, D))
+    sq = region(*lay["sq"], np.float32, (B * H, g))
+    qbar = region(qbar_off, B * H * g * D * 4, np.float32, (B * H, g, D))
+    comp = region(comp_off, B * H * g * npad * 4, np.float32, (B * H, g, npad))
+    for h in range(H):
+        qz = sage.quantise_head(inp["q"][0, h].double().numpy(), inp["k"][0, h].double().numpy(),
+                                inp["v"][0, h].double().numpy(), smooth_q=True)
+        assert np.array_equal(qbar[h], qz["qbar"]), "qbar"
+        assert np.array_equal(q8[h, :N], qz["q8"]) and not q8[h, N:].any(), "q8"
+        assert np.array_equal(sq[h], qz["sq"]), "sq"
+        want = (qz["comp"] * (w.scale * math.log2(math.e))).astype(np.float32)
+        got = comp[h, :, :N]
+        err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+        say(f"  head {h}: comp max|err| {err.max():.3e} (|comp| max {np.abs(want).max():.3e})")
+        assert np.all(err <= 2.0 ** -22 * np.abs(want.astype(np.float64)) + 1e-30), "comp"
+
+
+@pytest.mark.parametrize("keylen", [False, True])
+@pytest.mark.parametrize("pv", ["fp8", "16"])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_smooth_parity_small(dev, dt, pv, keylen):
+    for N in (1, 63, 64, 65, 129, 200, 1000):
+        w = Workload(92, f"int8-smooth-{dt}", dt, 2, 2, N, 128, k_offset_var=2.0)
+        inp = offset_queries(make_inputs(w), 4.0, N)
+        kl = torch.tensor([max(1, N // 3), N], dtype=torch.int32) if keylen else None
+        say(f"case smooth pv={pv} dt={dt} N={N} keylen={keylen}")
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        o, lse = fa.fwd_int8qk(q, k, v, key_len=None if kl is None else kl.to(dev), return_lse=True, pv=pv,
+                               smooth_q=True)
+        torch.cuda.synchronize()
+        qn, kn, vn = (inp[n].double().numpy() for n in ("q", "k", "v"))
+        ref, ref_lse = sage.emulate(qn, kn, vn, w.scale, fa.fa_int8qk_kv_block(), return_lse=True,
+                                    key_len=None if kl is None else kl.numpy(),
+                                    pv="fp8" if pv == "fp8" else dt, smooth_q=True)
+        got = o.cpu().double().numpy()
+        err = np.abs(got - ref)
+        say(f"  max|err|={err.max():.3e} mean|err|={err.mean():.3e}")
+        assert np.all(err <= 1e-2 + HALF_ULP[w.torch_dtype] * np.abs(ref))
+        assert err.mean() <= 1e-3
+        check_vs_emulation(got, ref, w.torch_dtype, f"N={N}")
+        un, _ = attention.naive(qn, kn, vn, w.scale, key_len=None if kl is None else kl.numpy())
+        cos = (got * un).sum() / np.linalg.norm(got) / np.linalg.norm(un)
+        say(f"  cosine vs unquantised {cos:.5f}")
+        assert cos >= 0.99
+        lg = lse.cpu().double().numpy()
+        assert np.array_equal(np.isneginf(lg), np.isneginf(ref_lse))
+        fin = np.isfinite(ref_lse)
+        assert np.abs(lg[fin] - ref_lse[fin]).max() < 1e-4
+
+
+def test_smooth_gain_on_offset_queries(dev):
+    """On queries with large per-block offsets the smoothed call is closer to
+    unquantised attention than the plain INT8 one (16-bit P V, so that Q K^T
+    quantisation is the main error); N = 5000 takes two 64-block tiles of the
+    compensation table and many key tiles."""
+    w = Workload(91, "int8-smooth-gain", "bf16", 1, 2, 5000, 128)
+    inp = offset_queries(make_inputs(w), 20.0, 7)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o_s = fa.fwd_int8qk(q, k, v, pv="16", smooth_q=True)
+    o_p = fa.fwd_int8qk(q, k, v, pv="16")
+    torch.cuda.synchronize()
+    rows = np.arange(0, 5000, 37)
+    e = {}
+    for name, o in (("smoothed", o_s), ("plain", o_p)):
+        tot = 0.0
+        for h in range(2):
+            qh, kh, vh = (inp[n][0, h].double().numpy() for n in ("q", "k", "v"))
+            un, _ = attention.rows(qh[rows], kh, vh, w.scale)
+            tot += ((o[0, h, rows].cpu().double().numpy() - un) ** 2).sum()
+        e[name] = np.sqrt(tot / (2 * len(rows) * 128))
+    say(f"  rms error vs unquantised: smoothed {e['smoothed']:.3e}, plain {e['plain']:.3e}")
+    assert e["smoothed"] < 0.5 * e["plain"]
+
+
+def test_smooth_fully_masked_and_additive_refused(dev):
+    w = Workload(90, "int8-smooth-mask", "bf16", 2, 2, 100, 128)
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = fa.fwd_int8qk(q, k, v, key_len=torch.tensor([0, 100], dtype=torch.int32, device=dev),
+                           return_lse=True, smooth_q=True)
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.isfinite(o[1]).all()
+    with pytest.raises(fa.FAError):
+        fa.fwd_int8qk(q, k, v, attn_mask=torch.zeros(1, 1, 100, 100, device=dev), smooth_q=True)

@@ -152,8 +152,8 @@ int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     return record_launch("fa_fwd_pp_kernel");
   } else if constexpr (D == 128 && sizeof(T) == 2) {
     // 16-bit, D = 128 with an additive mask: K/V staged by LDS DMA, 8 waves
-    // in step over 64-key tiles (one mask value is loaded per score; wider
-    // tiles exceed the register budget)
+    // in step over 64-key tiles (the mask values of a tile are read next to
+    // their use; wider tiles exceed the register budget)
     constexpr int NW = 8, BC = 64, MINB = 1;
     using C = fa::DmaCfg<T, BC, NW>;
     const int nqt = (Nq + C::BR - 1) / C::BR;

@@ -500,6 +500,8 @@ int int8qk_common(bool pv16, bool smooth, const void* q, const void* k, const vo
   if (smooth && kind == FA_MASK_ADDITIVE) return FA_ERR_UNSUPPORTED;
   if ((int64_t)(N + 256) * D * 2 > (int64_t)UINT32_MAX) return FA_ERR_SHAPE;
   const fa::Int8Layout lay = fa::int8qk_workspace_layout(B, H, N, D, pv16, smooth);
+  // one head's compensation table is addressed with 31-bit byte offsets
+  if (smooth && (uint64_t)lay.groups * (uint64_t)lay.npad * 4u >= (1ull << 31)) return FA_ERR_SHAPE;
   if (!workspace) return FA_ERR_WORKSPACE;
   if (workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return FA_ERR_ALIGN;

@@ -349,23 +349,28 @@ __global__ __launch_bounds__(256) void int8_quant_kernel(
 }
 
 // Q smoothing's compensation table, tile of 64 blocks x 64 keys per
-// workgroup of 256 threads: comp[bh][g][j] = fp32(c2 * sum_d qbar[g][d] *
+// workgroup of 4 waves: comp[bh][g][j] = fp32(c2 * sum_d qbar[g][d] *
 // Ks[j][d]) with Ks = fp32(K - kmean) (keys past N give 0) and c2 = scale *
-// log2(e), the products and sums in float64.  Each thread owns 4 blocks x 4
-// keys; LDS rows of 129 floats keep the 16 keys and the 4 blocks a wave
-// reads per channel on distinct banks.
+// log2(e), the products and sums in float64 on the matrix cores
+// (v_mfma_f64_16x16x4: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
+// and holds D[l / 16 + 4 r][l % 16] in its r-th double, as measured).  Wave w computes blocks
+// 32 (w & 1) + 0..31 against keys 32 (w >> 1) + 0..31 as 2 x 2 MFMA tiles.
+// qbar and Ks are staged in LDS as floats (exact in double), rows of 132 (a
+// 64-lane read of 16 rows x 4 channels then hits 64 distinct banks), 66 KB
+// per workgroup so that two share a CU and one's loads overlap the other's
+// MFMAs.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void int8_comp_kernel(
     const T* __restrict__ K, const float* __restrict__ kmean, const float* __restrict__ qbar,
     float* __restrict__ comp, int N, int npad, int groups, double c2) {
   static_assert(D == 128 && sizeof(T) == 2, "16-bit inputs, D = 128");
-  constexpr int RS = D + 1;
-  __shared__ float qs[64 * RS];
-  __shared__ float ks[64 * RS];
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  constexpr int RS = D + 4;
+  __shared__ __attribute__((aligned(16))) float qs[64 * RS];   // block means
+  __shared__ __attribute__((aligned(16))) float ks[64 * RS];   // K - kmean
   const int j0 = blockIdx.x * 64, g0 = blockIdx.y * 64, bh = blockIdx.z, t = threadIdx.x;
   const T* Kh = K + (size_t)bh * N * D;
   const float* km = kmean + (size_t)bh * D;
-  // stage: 64 rows x 16 chunks of 8 channels each, for K and for qbar
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int it = t + 256 * i, r = it / 16, c = it % 16;
@@ -382,35 +387,42 @@ __global__ __launch_bounds__(256) void int8_comp_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[e] = src[e];
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ks[r * RS + 8 * c + e] = kv[e];
-      qs[r * RS + 8 * c + e] = qv[e];
-    }
+    *reinterpret_cast<f32x4*>(ks + r * RS + 8 * c) = f32x4{kv[0], kv[1], kv[2], kv[3]};
+    *reinterpret_cast<f32x4*>(ks + r * RS + 8 * c + 4) = f32x4{kv[4], kv[5], kv[6], kv[7]};
+    *reinterpret_cast<f32x4*>(qs + r * RS + 8 * c) = f32x4{qv[0], qv[1], qv[2], qv[3]};
+    *reinterpret_cast<f32x4*>(qs + r * RS + 8 * c + 4) = f32x4{qv[4], qv[5], qv[6], qv[7]};
   }
   __syncthreads();
-  const int tg = t / 16, tj = t % 16;
-  double acc[4][4] = {};
-  for (int d = 0; d < D; ++d) {
-    double qd[4], kd[4];
+  const int lane = t & 63, wave = t >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  const int gb = 32 * (wave & 1), jb = 32 * (wave >> 1);
+  f64x4 acc[2][2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) qd[a] = (double)qs[(4 * tg + a) * RS + d];
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) kd[b] = (double)ks[(4 * tj + b) * RS + d];
+    for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int d0 = 0; d0 < D; d0 += 4) {
+    double av[2], bv[2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int x = 0; x < 2; ++x) av[x] = (double)qs[(gb + 16 * x + li) * RS + d0 + lk];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fma(qd[a], kd[b], acc[a][b]);
+    for (int y = 0; y < 2; ++y) bv[y] = (double)ks[(jb + 16 * y + li) * RS + d0 + lk];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int g = g0 + 4 * tg + a;
-    if (g < groups) {
-      const f32x4 w = {(float)(acc[a][0] * c2), (float)(acc[a][1] * c2), (float)(acc[a][2] * c2),
-                       (float)(acc[a][3] * c2)};
-      *reinterpret_cast<f32x4*>(comp + ((size_t)bh * groups + g) * npad + j0 + 4 * tj) = w;
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = g0 + gb + 16 * x + lk + 4 * r;
+      if (g < groups) {
+        float* dst = comp + ((size_t)bh * groups + g) * npad + j0 + jb + li;
+#pragma unroll
+        for (int y = 0; y < 2; ++y) dst[16 * y] = (float)(acc[x][y][r] * c2);
+      }
     }
-  }
 }
 
 // The QK^T accumulators start at the bit pattern of the float 1.5 * 2^23.  An
@@ -445,7 +457,10 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   constexpr int D = 128, BC = kInt8Bc, BR = 128, NT = 256;
   constexpr int KSTR = D;                       // int8 K row (128 bytes, chunks swizzled)
   constexpr int VSTR = BC;                      // e4m3 V^T row (64 keys, chunks swizzled)
-  constexpr int KBYTES = BC * KSTR, VBYTES = D * VSTR, BUF = KBYTES + VBYTES;
+  // SQ: the compensation rows of the workgroup's two query blocks travel with
+  // each tile (one 1 KB DMA instruction: 2 rows x 64 keys used)
+  constexpr int TBYTES = SQ ? 1024 : 0;
+  constexpr int KBYTES = BC * KSTR, VBYTES = D * VSTR, BUF = KBYTES + VBYTES + TBYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -484,10 +499,14 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     mvec = mask_rows_vec4(mask);
   }
   static_assert(!(SQ && MASK == kMaskAdd), "Q smoothing takes no additive mask");
-  if constexpr (SQ) {   // the compensation row of the wave's query block (rows are npad floats, aligned)
-    mrow = comp + ((size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)) * npad;
-    mvec = true;
-  }
+  // SQ: lanes 0-15 of wave 0 fetch 64 keys of the compensation row of block
+  // 2 qt, lanes 16-31 of block 2 qt + 1 (rows of npad floats); lanes 32-63,
+  // and blocks past the last, read out of range, which gives zeros
+  const uint32_t tbytes = SQ ? (uint32_t)groups * (uint32_t)npad * 4u : 0u;
+  const __amdgpu_buffer_rsrc_t tr =
+      make_rsrc(SQ ? static_cast<const void*>(comp + (size_t)bh * groups * npad) : static_cast<const void*>(k8), tbytes);
+  const int trs = lane >> 4;
+  const uint32_t toff = trs < 2 ? (uint32_t)(((2 * qt + trs) * npad + 4 * (lane & 15)) * 4) : kOobOffset;
   constexpr bool kRowTerm = SQ || MASK == kMaskAdd;   // a per-key term on every tile
 
   // Tiles reach LDS by buffer-load DMA (1 KB per instruction, two K and two
@@ -514,6 +533,11 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kb + (wave * 2 + i) * 1024), 16, koff[i] + krow, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vb + (wave * 2 + i) * 1024), 16, voff[i] + vcol, 0, 0, 0);
     }
+    if constexpr (SQ) {
+      if (wave == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, (lds_void*)(vb + VBYTES), 16, toff + (uint32_t)(j * BC) * 4u, 0, 0,
+                                                 0);
+    }
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -531,10 +555,31 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     // additive mask values of this lane's 32 keys (keys past N read -inf),
     // loaded ahead of the MFMAs (measured no faster issued before the DMA)
     float mk[32];
-    if constexpr (kRowTerm) load_mask_tile<2>(mk, mrow, SQ ? 1 : mask.sk, mvec, j * BC, n_eff, lh);
+    if constexpr (MASK == kMaskAdd) load_mask_tile<2>(mk, mrow, mask.sk, mvec, j * BC, n_eff, lh);
     const uint8_t* kb = smem + buf * BUF;
     const uint8_t* vb = kb + KBYTES;
     const int kv0 = j * BC;
+    if constexpr (SQ) {
+      // this wave's block row, staged with the tile: keys 32 G + 8 g + 4 lh + {0..3}
+      const float* trow = reinterpret_cast<const float*>(vb + VBYTES) + 64 * (wave >> 1);
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(trow + 32 * G + 8 * g + 4 * lh);
+          mk[16 * G + 4 * g] = x.x;
+          mk[16 * G + 4 * g + 1] = x.y;
+          mk[16 * G + 4 * g + 2] = x.z;
+          mk[16 * G + 4 * g + 3] = x.w;
+        }
+      if (kv0 + BC > n_eff) {                     // the ragged last tile: keys past n_eff drop out
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int key = kv0 + 32 * (i >> 4) + 8 * ((i & 15) >> 2) + 4 * lh + (i & 3);
+          if (key >= n_eff) mk[i] = -INFINITY;
+        }
+      }
+    }
     const float c = sq_w * skh[j] * c_log2;       // one K scale block per tile
 
     i32x16 si[2];

@@ -261,8 +261,9 @@ FA_API int fa_fwd_int8qk_pv16(const void* q, const void* k, const void* v, void*
  * without smoothing; with it, only each block's deviation from its mean is
  * quantised, which helps when query blocks share a large common offset.
  * lse as for fa_fwd_int8qk.  Masks: NONE or KEYLEN (ADDITIVE gives
- * FA_ERR_UNSUPPORTED); FA_ERR_ARG for pv16 outside {0, 1}; otherwise the
- * arguments and errors of fa_fwd_int8qk.
+ * FA_ERR_UNSUPPORTED); FA_ERR_ARG for pv16 outside {0, 1}; FA_ERR_SHAPE
+ * also when one head's table reaches 2^31 bytes (N above 185,344);
+ * otherwise the arguments and errors of fa_fwd_int8qk.
  *   workspace  at least fa_fwd_int8qk_smooth_workspace_bytes(B,H,N,D,pv16)
  *              bytes, 256-byte aligned: the regions of the chosen form's
  *              workspace, then

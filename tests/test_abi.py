@@ -263,3 +263,12 @@ def test_int8qk_smooth_validation(lib):
     assert call(pv16=1) == fa.FA_ERR_WORKSPACE          # the 16-bit form's workspace is larger
     assert call(ws=P + 16) == fa.FA_ERR_ALIGN
     assert call(N=1 << 24) == fa.FA_ERR_SHAPE
+
+
+def test_int8qk_smooth_table_limit(lib):
+    """One head's compensation table stays under 2^31 bytes: N = 185,344 is
+    accepted as far as the workspace check, one 64-token block more is not."""
+    def call(N):
+        return fa.fa_fwd_int8qk_smooth(P, P, P, P, None, None, 1, 1, N, 128, 0.1, fa.FA_BF16, 0, P, 0, None)
+    assert call(185344) == fa.FA_ERR_WORKSPACE
+    assert call(185345) == fa.FA_ERR_SHAPE

@@ -498,6 +498,7 @@ int int8qk_common(bool pv16, bool smooth, const void* q, const void* k, const vo
   if (D != 128) return FA_ERR_UNSUPPORTED;
   const int kind = mask ? mask->kind : FA_MASK_NONE;
   if (smooth && kind == FA_MASK_ADDITIVE) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > 65535) return FA_ERR_SHAPE;   // the prepass grids take B*H as a grid dimension
   if ((int64_t)(N + 256) * D * 2 > (int64_t)UINT32_MAX) return FA_ERR_SHAPE;
   const fa::Int8Layout lay = fa::int8qk_workspace_layout(B, H, N, D, pv16, smooth);
   // one head's compensation table is addressed with 31-bit byte offsets

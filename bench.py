@@ -14,10 +14,10 @@ N=119056, D=128, no mask, 4 outlier K channels scaled by 8).  The metric is
 attention TFLOP/s = 4*B*H*N^2*D / t.  Unless --no-extra is given the line
 also carries, under "extra", the FLUX-1024^2 layer, the SD1.5 768^2 layer
 with its key lengths (nominal and effective rates) and the Wan 2.1 layer
-through the INT8-QK / FP8-PV entry point next to the bf16 kernel (and the
-INT8-QK / 16-bit-PV form) on the same inputs, each comparison timed in
-interleaved rounds (medians); --extra adds the
-cross-attention, window-attention and merge workloads.
+through the INT8-QK / FP8-PV entry point next to the bf16 kernel, the
+INT8-QK / 16-bit-PV form and Q smoothing on the same inputs, each comparison
+timed in interleaved rounds (medians); --extra adds the cross-attention,
+window-attention and merge workloads.
 """
 from __future__ import annotations
 
@@ -223,7 +223,7 @@ def main() -> int:
             del inp
         return cache[key]
 
-    def measure(w, steps, warmup, split=True, quantised=None, pv16=None):
+    def measure(w, steps, warmup, split=True, quantised=None, pv16=None, smooth=False):
         quantised = w.quantised if quantised is None else quantised
         pv16 = w.pv16 if pv16 is None else pv16
         if w.merge:
@@ -238,10 +238,15 @@ def main() -> int:
         q, k, v, kl = d["q"], d["k"], d["v"], d["key_len"]
         o = torch.empty_like(q)
         if quantised:
-            size = fa.fa_fwd_int8qk_pv16_workspace_bytes if pv16 else fa.fa_fwd_int8qk_workspace_bytes
-            ws = torch.empty(size(w.B, w.H, w.N, w.D), dtype=torch.uint8, device=dev)
+            if smooth:
+                nbytes = fa.fa_fwd_int8qk_smooth_workspace_bytes(w.B, w.H, w.N, w.D, 1 if pv16 else 0)
+            else:
+                size = fa.fa_fwd_int8qk_pv16_workspace_bytes if pv16 else fa.fa_fwd_int8qk_workspace_bytes
+                nbytes = size(w.B, w.H, w.N, w.D)
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
             pv = "16" if pv16 else "fp8"
-            call = lambda: fa.fwd_int8qk(q, k, v, key_len=kl, workspace=ws, out=o, pv=pv)  # noqa: E731
+            call = lambda: fa.fwd_int8qk(q, k, v, key_len=kl, workspace=ws, out=o, pv=pv,  # noqa: E731
+                                         smooth_q=smooth)
         else:
             call = lambda: fa.fwd(q, k, v, key_len=kl, out=o, split=split)  # noqa: E731
         return timed(call, steps, warmup)
@@ -361,7 +366,8 @@ def main() -> int:
             steps, warm = (5, 1) if big else (50, 5)
             if wx.quantised:
                 # the three forms on the same device inputs, interleaved
-                e_ms, b_ms, p_ms = interleaved(wx, [{}, {"quantised": False}, {"pv16": True}], 2, 3, 1)
+                e_ms, b_ms, p_ms, s_ms = interleaved(wx, [{}, {"quantised": False}, {"pv16": True}, {"smooth": True}],
+                                                     2, 3, 1)
                 rec = {"int8qk_ms": round(e_ms, 4), "int8qk_tops": round(fl / (e_ms * 1e-3) / 1e12, 2),
                        "entry": "fa_fwd_int8qk (prepass kernels included)",
                        "bf16_same_inputs_ms": round(b_ms, 3),
@@ -369,7 +375,9 @@ def main() -> int:
                        "int8qk_speedup_vs_bf16": round(b_ms / e_ms, 3),
                        "int8qk_pv16_ms": round(p_ms, 3),
                        "int8qk_pv16_tops": round(fl / (p_ms * 1e-3) / 1e12, 2),
-                       "int8qk_pv16_speedup_vs_bf16": round(b_ms / p_ms, 3)}
+                       "int8qk_pv16_speedup_vs_bf16": round(b_ms / p_ms, 3),
+                       "int8qk_smooth_ms": round(s_ms, 3),
+                       "int8qk_smooth_speedup_vs_bf16": round(b_ms / s_ms, 3)}
             elif takes_split(wx):
                 e_ms, u_ms = interleaved(wx, [{}, {"split": False}], 6, steps, warm)
                 rec = {"ms": round(e_ms, 4), "tflops": round(fl / (e_ms * 1e-3) / 1e12, 2), "entry": "fa_fwd_ws",

@@ -197,7 +197,9 @@ FA_API int fa_fwd_ws_static(const void* q, const void* k, const void* v, void* o
  * lse (if requested) is that of the smoothed, quantised scores in step 4: it
  * differs from the unquantised row log-sum-exp by -scale * q . kmean (the
  * per-row constant smoothing removes) plus quantisation error.
- * Same tensor conventions as fa_fwd.  dtype F16 or BF16, D = 128.  Masks
+ * Same tensor conventions as fa_fwd.  dtype F16 or BF16, D = 128, B*H at
+ * most 65535 (FA_ERR_SHAPE beyond: the prepass grids take B*H as a
+ * dimension).  Masks
  * act after quantisation (kmean and the scales still run over all N
  * tokens): KEYLEN drops keys beyond the length; ADDITIVE (strides as in
  * fa_fwd) adds its float32 value to the dequantised, scaled score of step 4,

@@ -272,3 +272,15 @@ def test_int8qk_smooth_table_limit(lib):
         return fa.fa_fwd_int8qk_smooth(P, P, P, P, None, None, 1, 1, N, 128, 0.1, fa.FA_BF16, 0, P, 0, None)
     assert call(185344) == fa.FA_ERR_WORKSPACE
     assert call(185345) == fa.FA_ERR_SHAPE
+
+
+def test_int8qk_batch_head_limit(lib):
+    """B*H above 65535 is refused before any launch, by every quantised entry point."""
+    ws = fa.fa_fwd_int8qk_workspace_bytes(1, 1, 64, 128)
+    assert fa.fa_fwd_int8qk(P, P, P, P, None, None, 2, 32768, 64, 128, 0.1, fa.FA_BF16, P, ws, None) == fa.FA_ERR_SHAPE
+    assert fa.fa_fwd_int8qk_pv16(P, P, P, P, None, None, 65536, 1, 64, 128, 0.1, fa.FA_BF16, P, ws,
+                                 None) == fa.FA_ERR_SHAPE
+    assert fa.fa_fwd_int8qk_smooth(P, P, P, P, None, None, 256, 257, 64, 128, 0.1, fa.FA_BF16, 0, P, ws,
+                                   None) == fa.FA_ERR_SHAPE
+    # 65535 itself passes the shape checks (and fails on the tiny workspace)
+    assert fa.fa_fwd_int8qk(P, P, P, P, None, None, 5, 13107, 64, 128, 0.1, fa.FA_BF16, P, ws, None) == fa.FA_ERR_WORKSPACE

@@ -36,7 +36,8 @@
 // phase, where its wave would otherwise idle at the barrier: group A reads
 // V(t) in phase 2t + 1, group B in phase 2t + 2, both after V(t) landed (end
 // of phase 2t).  A prologue loads K(0) with all eight waves; group B loads
-// V(0) in phase 0.
+// V(0) in phase 0 and waits for it before phase 0 ends, since group A reads
+// it at the end of phase 1.
 //
 // The ragged last tile (keys [nfull BC, n_eff)) is processed first with all
 // eight waves in step, so the phase loop sees only full tiles.
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
         dma4(kr, kbuf(t + 1), t + 1, ks, offs);
         softmax_phase(t, BoolTag<false>{});
         __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
-        vread_first(vbuf(t));                                   // V(t): landed in phase 2t
+        vread_first(vbuf(t));                                   // V(t): landed by phase 2t (V(0): phase 0)
         lds_barrier();                                          // phase 2t + 1
         mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
         lds_barrier();                                          // phase 2t + 2
@@ -452,9 +453,11 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
       lds_barrier();                                            // phase 2nt + 1
     } else {
       dma4(vr, vbuf(0), 0, vs, offs);                           // V(0), buffer unused yet
+      // V(0) must be resident by the end of phase 0: group A pre-reads it
+      // at the end of its first softmax phase, phase 1
+      __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): V(0) landed
       lds_barrier();                                            // phase 0
       mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
-      __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): V(0) landed
       lds_barrier();                                            // phase 1
       for (int t = 0; t + 1 < nt; ++t) {
         // phase 2t + 2: V(t + 1), first read at the end of phase 2t + 3,

@@ -56,7 +56,11 @@ def check_o(o_gpu, o_ref, dtype, what):
     rel = np.sqrt((err ** 2).mean() / max((o_ref ** 2).mean(), 1e-300))
     say(f"  {what}: max|err|={err.max():.3e} mean|err|={err.mean():.3e} relRMS={rel:.3e}")
     assert np.isfinite(o).all(), what
-    assert np.all(err <= mx + HALF_ULP[dtype] * np.abs(o_ref)), what
+    bad = err > mx + HALF_ULP[dtype] * np.abs(o_ref)
+    if bad.any():                               # name the failing rows before failing
+        rows = np.argwhere(bad.any(axis=-1))
+        say(f"  {what}: {len(rows)} rows out of bounds, first (b, h, row): {rows[:12].tolist()}")
+    assert not bad.any(), what
     if mean_tol is not None:
         assert err.mean() <= mean_tol, what
 

@@ -70,9 +70,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
     int H, int Nq, int Nk, int nqt, float c_log2) {
   using C = DmaCfg<T, BC, NW>;
   constexpr int D = C::D;
-  // K0 K1 V0 V1, then (additive masks) two 64-key segments of a mask row
-  constexpr int MROW = (MASK == kMaskAdd) ? 2 * BC * 4 : 0;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE + MROW];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];   // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -107,27 +105,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
     *reinterpret_cast<u32x4*>(smem + 2 * C::TILE + 16 * i) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  constexpr bool kPre = (MASK == kMaskAdd);
-  // additive mask: this lane's query row (row 0 stands in for rows past Nq,
-  // whose results are not stored)
-  const float* mrow = nullptr;
-  bool mvec = false;
-  // A key-contiguous mask shared by every query of the head (stride_q 0: a
-  // key-padding bias) travels with the tiles instead: one 4-byte-per-lane DMA
-  // of wave 0 brings the tile's 64 values into LDS (keys past Nk read 0 and
-  // are dropped at use), so its loads never stall the score computation.
-  bool mstage = false;
-  const float* mbase = nullptr;
-  if constexpr (kPre) {
-    mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh +
-           (int64_t)(q_ok ? q_row : 0) * mask.sq;
-    mvec = mask_rows_vec4(mask);
-    mstage = mask.sq == 0 && mask.sk == 1;
-    mbase = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh;
-  }
-  const __amdgpu_buffer_rsrc_t mr = make_rsrc(kPre ? static_cast<const void*>(mbase) : static_cast<const void*>(K),
-                                              kPre ? (uint32_t)Nk * 4u : 0u);
-
   // DMA of tile j into buffer j & 1.  Instruction i of this wave fills LDS
   // kilobyte (wave * DMA_PER_WAVE + i): rows 4 per kilobyte, this lane's
   // 16 bytes at row r, physical chunk lane % 16.
@@ -145,11 +122,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kb + kb_idx * 1024), 16, koff, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vb + kb_idx * 1024), 16, voff, 0, 0, 0);
     }
-    if constexpr (kPre) {
-      if (mstage && wave == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(mr, (lds_void*)(smem + 4 * C::TILE + (j & 1) * BC * 4), 4,
-                                                 (row0 + (uint32_t)lane) * 4u, 0, 0, 0);
-    }
   };
   // Wait for this wave's DMA, then for everyone's.
   auto dma_wait_barrier = [&]() {
@@ -166,7 +138,17 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[p][i] = 0.f;
 
+  constexpr bool kPre = (MASK == kMaskAdd);
   const float cs = kPre ? 1.f : c_log2;
+  // additive mask: this lane's query row (row 0 stands in for rows past Nq,
+  // whose results are not stored)
+  const float* mrow = nullptr;
+  bool mvec = false;
+  if constexpr (kPre) {
+    mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh +
+           (int64_t)(q_ok ? q_row : 0) * mask.sq;
+    mvec = mask_rows_vec4(mask);
+  }
 
   auto step = [&](int j, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -215,28 +197,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void fa_fwd_dma_kernel(
               for (int r = 0; r < 4; ++r) s[G][4 * g + r] = __builtin_fmaf(s[G][4 * g + r], c_log2, mq[r] * kLog2e);
             }
         };
-        if (mstage) {
-          const float* ml = reinterpret_cast<const float*>(smem + 4 * C::TILE + (j & 1) * BC * 4);
-#pragma unroll
-          for (int G = 0; G < C::SB; ++G)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 mq = *reinterpret_cast<const f32x4*>(ml + 32 * G + 8 * g + 4 * lh);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) s[G][4 * g + r] = __builtin_fmaf(s[G][4 * g + r], c_log2, mq[r] * kLog2e);
-            }
-          if (kv0 + BC > Nk) {                    // the ragged last tile: keys past Nk drop out
-#pragma unroll
-            for (int G = 0; G < C::SB; ++G)
-#pragma unroll
-              for (int i = 0; i < 16; ++i)
-                if (kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3) >= Nk) s[G][i] = -INFINITY;
-          }
-        } else if (mvec && kv0 + BC <= Nk) {
-          add_mask(BoolTag<true>{});
-        } else {
-          add_mask(BoolTag<false>{});
-        }
+        if (mvec && kv0 + BC <= Nk) add_mask(BoolTag<true>{});
+        else add_mask(BoolTag<false>{});
       } else {
 #pragma unroll
         for (int G = 0; G < C::SB; ++G)

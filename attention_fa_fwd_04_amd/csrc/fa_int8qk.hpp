@@ -459,10 +459,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   constexpr int VSTR = BC;                      // e4m3 V^T row (64 keys, chunks swizzled)
   // SQ: the compensation rows of the workgroup's two query blocks travel with
   // each tile (one 1 KB DMA instruction: 2 rows x 64 keys used)
-  // An additive mask shared by every query of the head (stride_q 0,
-  // key-contiguous) travels the same way: 64 values per tile, one 4-byte
-  // DMA per lane of wave 0.
-  constexpr int TBYTES = (SQ || MASK == kMaskAdd) ? 1024 : 0;
+  constexpr int TBYTES = SQ ? 1024 : 0;
   constexpr int KBYTES = BC * KSTR, VBYTES = D * VSTR, BUF = KBYTES + VBYTES + TBYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
 
@@ -505,14 +502,9 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   // SQ: lanes 0-15 of wave 0 fetch 64 keys of the compensation row of block
   // 2 qt, lanes 16-31 of block 2 qt + 1 (rows of npad floats); lanes 32-63,
   // and blocks past the last, read out of range, which gives zeros
-  bool mstage = false;
-  if constexpr (MASK == kMaskAdd) mstage = mask.sq == 0 && mask.sk == 1;
-  const uint32_t tbytes = SQ ? (uint32_t)groups * (uint32_t)npad * 4u : (MASK == kMaskAdd ? (uint32_t)N * 4u : 0u);
-  const void* tbase = SQ ? static_cast<const void*>(comp + (size_t)bh * groups * npad)
-                         : (MASK == kMaskAdd ? static_cast<const void*>(reinterpret_cast<const float*>(mask.ptr) +
-                                                                        b * mask.sb + h * mask.sh)
-                                             : static_cast<const void*>(k8));
-  const __amdgpu_buffer_rsrc_t tr = make_rsrc(tbase, tbytes);
+  const uint32_t tbytes = SQ ? (uint32_t)groups * (uint32_t)npad * 4u : 0u;
+  const __amdgpu_buffer_rsrc_t tr =
+      make_rsrc(SQ ? static_cast<const void*>(comp + (size_t)bh * groups * npad) : static_cast<const void*>(k8), tbytes);
   const int trs = lane >> 4;
   const uint32_t toff = trs < 2 ? (uint32_t)(((2 * qt + trs) * npad + 4 * (lane & 15)) * 4) : kOobOffset;
   constexpr bool kRowTerm = SQ || MASK == kMaskAdd;   // a per-key term on every tile
@@ -545,10 +537,6 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
       if (wave == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, (lds_void*)(vb + VBYTES), 16, toff + (uint32_t)(j * BC) * 4u, 0, 0,
                                                  0);
-    } else if constexpr (MASK == kMaskAdd) {
-      if (mstage && wave == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, (lds_void*)(vb + VBYTES), 4, (uint32_t)(j * BC + lane) * 4u, 0, 0,
-                                                 0);
     }
   };
 
@@ -567,16 +555,13 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
     // additive mask values of this lane's 32 keys (keys past N read -inf),
     // loaded ahead of the MFMAs (measured no faster issued before the DMA)
     float mk[32];
+    if constexpr (MASK == kMaskAdd) load_mask_tile<2>(mk, mrow, mask.sk, mvec, j * BC, n_eff, lh);
     const uint8_t* kb = smem + buf * BUF;
     const uint8_t* vb = kb + KBYTES;
     const int kv0 = j * BC;
-    if constexpr (MASK == kMaskAdd) {
-      if (!mstage) load_mask_tile<2>(mk, mrow, mask.sk, mvec, j * BC, n_eff, lh);
-    }
-    if (SQ || mstage) {
-      // the row staged with the tile (SQ: this wave's query block; a shared
-      // mask: row 0): keys 32 G + 8 g + 4 lh + {0..3}
-      const float* trow = reinterpret_cast<const float*>(vb + VBYTES) + (SQ ? 64 * (wave >> 1) : 0);
+    if constexpr (SQ) {
+      // this wave's block row, staged with the tile: keys 32 G + 8 g + 4 lh + {0..3}
+      const float* trow = reinterpret_cast<const float*>(vb + VBYTES) + 64 * (wave >> 1);
 #pragma unroll
       for (int G = 0; G < 2; ++G)
 #pragma unroll

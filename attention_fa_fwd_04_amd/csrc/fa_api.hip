@@ -14,6 +14,7 @@
 #include "fa_fwd_dma.hpp"
 #include "fa_fwd_pp.hpp"
 #include "fa_int8qk.hpp"
+#include "fa_int8qk_pv16_pp.hpp"
 #include "fa_merge.hpp"
 #include "fa_probe.hpp"
 

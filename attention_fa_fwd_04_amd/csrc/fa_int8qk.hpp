@@ -709,7 +709,7 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
 // the running max) and V^T read unquantised from the workspace (keys permuted
 // per 32 by v16_pos); P V runs on the 16-bit 32x32x16 MFMA, four per 32
 // channels per 64-key tile.  Launched for additive masks and Q smoothing;
-// other calls take the phase-alternating fa_int8qk_pv16_pp_kernel.
+// other calls take the phase-alternating fa_int8qk_pv16_pp_kernel (same V^T).
 template <typename T, int MASK, bool SQ>
 __global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const T* __restrict__ vt,
@@ -937,10 +937,9 @@ struct Int8Ops {
   float *sq, *sk, *sv, *comp;
 };
 
-// with_vt = false skips the V^T slice (a main kernel that reads V itself).
 template <typename T, bool PV16>
 Int8Ops int8_prepass(const void* q, const void* k, const void* v, int B, int H, int N, float scale, void* workspace,
-                     const Int8Layout& L, bool smooth, hipStream_t st, bool with_vt = true) {
+                     const Int8Layout& L, bool smooth, hipStream_t st) {
   constexpr int D = 128;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   Int8Ops op{reinterpret_cast<int8_t*>(ws + L.q8), reinterpret_cast<int8_t*>(ws + L.k8), ws + L.v8t,
@@ -958,14 +957,13 @@ Int8Ops int8_prepass(const void* q, const void* k, const void* v, int B, int H, 
   hipLaunchKernelGGL((int8_stats_kernel<T, D>), dim3(L.splits, BH), dim3(256), 0, st, K, V, kpart, vpart, N, L.splits,
                      L.split_rows);
   hipLaunchKernelGGL((int8_finalize_kernel<D>), dim3(BH), dim3(D), 0, st, kpart, vpart, kmean, op.sv, vmul, N, L.splits);
-  const int slices = with_vt ? 3 : 2;   // Q, K (and V)
   if (smooth) {
-    hipLaunchKernelGGL((int8_quant_kernel<T, D, PV16, true>), dim3(L.groups, BH, slices), dim3(256), 0, st, Q, K, V,
+    hipLaunchKernelGGL((int8_quant_kernel<T, D, PV16, true>), dim3(L.groups, BH, 3), dim3(256), 0, st, Q, K, V,
                        kmean, vmul, op.q8, op.k8, op.vt, op.sq, op.sk, qbar, N, L.npad, L.groups);
     hipLaunchKernelGGL((int8_comp_kernel<T, D>), dim3(L.npad / 64, (L.groups + 63) / 64, BH), dim3(256), 0, st, K,
                        kmean, qbar, op.comp, N, L.npad, L.groups, (double)scale * 1.4426950408889634);
   } else {
-    hipLaunchKernelGGL((int8_quant_kernel<T, D, PV16, false>), dim3(L.groups, BH, slices), dim3(256), 0, st, Q, K, V,
+    hipLaunchKernelGGL((int8_quant_kernel<T, D, PV16, false>), dim3(L.groups, BH, 3), dim3(256), 0, st, Q, K, V,
                        kmean, vmul, op.q8, op.k8, op.vt, op.sq, op.sk, nullptr, N, L.npad, L.groups);
   }
   return op;

@@ -9,7 +9,7 @@
 // for the P V MFMA; l sums the unrounded P; O = acc / l.  Tiles are visited
 // in key order, the ragged last tile last, so every P is rounded against the
 // same running max as there; only the fp32 accumulation order inside P V
-// differs.  V is read from the caller's tensor (not the prepass's V^T copy).
+// differs.
 // No additive mask and no Q smoothing (those take fa_int8qk_pv16_kernel); a
 // key-length mask shortens the key range.
 //
@@ -23,10 +23,13 @@
 // phase.  The MFMA phase (768 matrix-core cycles) is the longer one, as in
 // the bf16 kernel.
 //
-// Tiles.  An int8 K tile (64 rows x 128 bytes, 8 KB, the chunk swizzle of
-// fa_int8qk_kernel) and a 16-bit V tile (64 rows x 256 bytes, 16 KB, the
-// swizzle v_swz of fa_fwd_dma.hpp, read with transposing LDS reads): two of
-// each, filled by buffer-load DMA.  Group A loads K(t+1) at the start of its
+// Tiles.  An int8 K tile (64 rows x 128 bytes, 8 KB) and a 16-bit V^T tile
+// from the prepass (128 channel rows x 64 keys, 128 bytes, 16 KB), both with
+// the chunk swizzle (r / 2) % 8 of 128-byte rows: two of each, filled by
+// buffer-load DMA.  V^T rows are read with ds_read_b128 (one 16-byte operand
+// chunk per lane and MFMA), not with transposing reads of V rows, which
+// move half the bytes per LDS instruction: the LDS would otherwise issue
+// more cycles than the matrix core per phase.  Group A loads K(t+1) at the start of its
 // softmax phase 2t + 1 (two 1 KB instructions per wave), group B loads
 // V(t+1) at the start of its softmax phase 2t + 2 (four per wave); each
 // waits for its own DMA before the phase's closing barrier, and buffer
@@ -41,13 +44,13 @@ namespace fa {
 
 template <typename T, int MASK>
 __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
-    const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const T* __restrict__ V,
+    const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const T* __restrict__ vt,
     const float* __restrict__ sq, const float* __restrict__ sk, MaskArgs mask, T* __restrict__ O,
     float* __restrict__ LSE, int H, int N, int npad, int groups, int nqt, float c_log2) {
   constexpr int D = 128, BC = kInt8Bc, BR = 256;
   constexpr int KBYTES = BC * D;                // int8 K tile, 128-byte rows
-  constexpr int VROW = 2 * D;                   // 16-bit V row, 256 bytes
-  constexpr int VBYTES = BC * VROW;
+  constexpr int VROW = 2 * BC;                  // 16-bit V^T row (64 keys), 128 bytes
+  constexpr int VBYTES = D * VROW;
   static_assert(KBYTES == 8192 && VBYTES == 16384, "8 and 16 DMA instructions per tile");
   static_assert(MASK != kMaskAdd, "additive masks take fa_int8qk_pv16_kernel");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KBYTES + 2 * VBYTES];   // K0 K1 V0 V1
@@ -70,8 +73,8 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
 
   const int8_t* Qh = q8 + (size_t)bh * npad * D;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(k8 + (size_t)bh * npad * D, (uint32_t)npad * D);
-  // V rows at or past n_eff read as zero
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + (size_t)bh * N * D, (uint32_t)n_eff * VROW);
+  // V^T [D, npad] in the prepass's key order; keys past N are zero there
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vt + (size_t)bh * D * npad, (uint32_t)D * npad * 2);
 
   const int q_row = qt * BR + wave * 32 + ln;
   const bool q_ok = q_row < N;
@@ -84,17 +87,16 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
   const float sq_w = sq[(size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)];
   const float* skh = sk + (size_t)bh * groups;
 
-  // DMA offsets (tile 0) of 1 KB block kb: K rows 8 kb + lane / 8, chunk
-  // lane % 8 fetching logical chunk (lane % 8) ^ ((r / 2) % 8); V rows
-  // 4 kb + lane / 16, chunk lane % 16 fetching (lane % 16) ^ v_swz(r).
-  const int k_r0 = lane >> 3, v_r0 = lane >> 4;
+  // DMA offsets (tile 0) of 1 KB block kb: rows 8 kb + lane / 8 (of K, or
+  // of V^T), chunk lane % 8 fetching logical chunk (lane % 8) ^ ((r / 2) % 8).
+  const int k_r0 = lane >> 3;
   auto koff = [&](int kb) -> uint32_t {
     const int r = kb * 8 + k_r0;
     return (uint32_t)r * D + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) << 4);
   };
   auto voff = [&](int kb) -> uint32_t {
-    const int r = kb * 4 + v_r0;
-    return (uint32_t)r * VROW + (uint32_t)(((lane & 15) ^ v_swz(r)) << 4);
+    const int r = kb * 8 + k_r0;
+    return (uint32_t)r * (uint32_t)npad * 2u + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) << 4);
   };
   uint8_t* const kbuf0 = smem;
   uint8_t* const vbuf0 = smem + 2 * KBYTES;
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
                                              0, 0, 0);
   };
   auto dma_v_all = [&](int j, uint8_t* buf) {
-    const uint32_t row_off = (uint32_t)(j * BC) * VROW;
+    const uint32_t row_off = (uint32_t)(j * BC) * 2u;          // tile j: keys 64 j.. of every row
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(buf + 2 * wave * 1024), 16, v_all0 + row_off, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(buf + (2 * wave + 1) * 1024), 16, v_all1 + row_off, 0, 0,
                                              0);
@@ -118,18 +120,13 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
   uint32_t k_off[4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) k_off[st] = (uint32_t)ln * D + (uint32_t)((((2 * st + lh) ^ ((ln >> 1) & 7))) << 4);
-  // V operands (transposing reads): this lane, as source lane 4k + t of its
-  // 16-lane group, fetches channels 4t..4t+3 of key k (keys +0..3, then
-  // +8..11).  Row r = 32 G + 16 cc + 4 lh + gk (+ 8) has swizzle
-  // v_swz(4 lh + gk): G, cc and the +8 only add constant row offsets.
+  // V^T operands: P V step k (key block G = k / 2, half cc = k % 2) reads
+  // row 32 p + ln, logical chunk 4 G + 2 lh + cc (the prepass's key order
+  // puts there the 8 keys of this lane's P^T chunk), swizzle (ln / 2) % 8.
   uint32_t vaddr[4];
-  {
-    const int gk = (lane & 15) >> 2, gt = lane & 3, ga = (lane >> 4) & 1;
-    const int r_l = 4 * (lane >> 5) + gk;
-    const uint32_t vbase = (uint32_t)r_l * VROW + (uint32_t)((gt & 1) << 3);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) vaddr[p] = vbase + (uint32_t)(((4 * p + 2 * ga + (gt >> 1)) ^ v_swz(r_l)) << 4);
-  }
+  for (int k = 0; k < 4; ++k)
+    vaddr[k] = (uint32_t)ln * VROW + (uint32_t)(((4 * (k >> 1) + 2 * lh + (k & 1)) ^ ((ln >> 1) & 7)) << 4);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc[4];
@@ -143,16 +140,8 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
 
   auto vread = [&](const uint8_t* vb, auto kk) {
     constexpr int k = decltype(kk)::value;
-    constexpr int off = (32 * (k >> 1) + 16 * (k & 1)) * VROW;
-    static_for<4>([&](auto pp) {
-      constexpr int p = decltype(pp)::value;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[p] + off));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + vaddr[p] + off + 8 * VROW));
-      va[k % 2][p].x = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
-      va[k % 2][p].y = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
-      va[k % 2][p].z = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
-      va[k % 2][p].w = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
-    });
+#pragma unroll
+    for (int p = 0; p < 4; ++p) va[k % 2][p] = *reinterpret_cast<const u32x4*>(vb + p * 32 * VROW + vaddr[k]);
   };
   auto vread_first = [&](const uint8_t* vb) { vread(vb, std::integral_constant<int, 0>{}); };
 
@@ -283,7 +272,7 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
                                                  0, 0);
     };
     auto dma_v = [&](uint8_t* buf, int j) {
-      const uint32_t row_off = (uint32_t)(j * BC) * VROW;
+      const uint32_t row_off = (uint32_t)(j * BC) * 2u;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(buf + (4 * w4 + i) * 1024), 16, offs[i] + row_off, 0,
@@ -365,19 +354,17 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
 }
 
 // The 16-bit-PV form: the phase-alternating kernel for full runs of key
-// tiles without a per-key term (no mask or a key length), reading V from the
-// caller's tensor; fa_int8qk_pv16_kernel takes additive masks and Q
-// smoothing, with V^T from the prepass.
+// tiles without a per-key term (no mask or a key length);
+// fa_int8qk_pv16_kernel takes additive masks and Q smoothing.
 template <typename T>
 int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse, int mask_kind, MaskArgs m,
                        int B, int H, int N, float scale, void* workspace, const Int8Layout& L, bool smooth,
                        hipStream_t st) {
-  const bool pp = !smooth && mask_kind != kMaskAdd;
-  const Int8Ops op = int8_prepass<T, true>(q, k, v, B, H, N, scale, workspace, L, smooth, st, !pp);
-  if (pp) {
+  const Int8Ops op = int8_prepass<T, true>(q, k, v, B, H, N, scale, workspace, L, smooth, st);
+  if (!smooth && mask_kind != kMaskAdd) {
     const int nqt = (N + 255) / 256;
     const dim3 grid(B * H * nqt), block(512);
-    const T* V = static_cast<const T*>(v);
+    const T* V = static_cast<const T*>(op.vt);
     if (mask_kind == kMaskLen)
       hipLaunchKernelGGL((fa_int8qk_pv16_pp_kernel<T, kMaskLen>), grid, block, 0, st, op.q8, op.k8, V, op.sq, op.sk,
                          m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);

@@ -240,9 +240,7 @@ FA_API int fa_fwd_int8qk(const void* q, const void* k, const void* v, void* o, f
  * (fa_fwd_int8qk_pv16_workspace_bytes) has the same regions in the same
  * order except v8t, which holds V^T in `dtype`: [BH, D, Np], row d,
  * position 64g + 32(k >> 5) + pi16(k & 31) holds key 64g + k,
- * pi16(k) = 16*((k>>2)&1) + 4*(k>>3) + (k&3).  The v8t region is written
- * only by calls with an additive mask; without a mask or with a key-length
- * mask the main loop reads V from `v` directly and leaves v8t as it was.
+ * pi16(k) = 16*((k>>2)&1) + 4*(k>>3) + (k&3).
  */
 FA_API size_t fa_fwd_int8qk_pv16_workspace_bytes(int B, int H, int N, int D);
 FA_API int fa_fwd_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -224,18 +224,10 @@ def test_pv16_operands_bit_exact(dev, dt):
     w = WORKLOADS[5].with_shape(H=2, N=1000, dtype=dt)
     inp = make_inputs(w)
     B, H, N, D = w.B, w.H, w.N, w.D
-    lay, npad = layout(B, H, N, D, vbytes=2)
-    ws = torch.full((fa.fa_fwd_int8qk_pv16_workspace_bytes(B, H, N, D),), 0xA5, dtype=torch.uint8, device=dev)
-    # without a mask the main loop reads V itself: the V^T slice is skipped
+    ws = torch.empty(fa.fa_fwd_int8qk_pv16_workspace_bytes(B, H, N, D), dtype=torch.uint8, device=dev)
     run(dev, inp, ws=ws, pv="16")
-    off, nbytes = lay["v8t"]
-    assert bool((ws[off:off + nbytes] == 0xA5).all()), "V^T written by a call that does not read it"
-    # an additive mask takes the kernel that reads V^T from the workspace
-    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
-    zero = torch.zeros((1, 1, 1, N), dtype=torch.float32, device=dev)
-    fa.fwd_int8qk(q, k, v, attn_mask=zero, workspace=ws, pv="16")
-    torch.cuda.synchronize()
     buf = ws.cpu().numpy()
+    lay, npad = layout(B, H, N, D, vbytes=2)
 
     def region(name, dtype, shape):
         off, nbytes = lay[name]

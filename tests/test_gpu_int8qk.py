@@ -178,6 +178,41 @@ def test_int8qk_parity_small(dev, dt, keylen):
         assert np.abs(lg[fin] - ref_lse[fin]).max() < 1e-4
 
 
+@pytest.mark.parametrize("pv", ["fp8", "16"])
+def test_degenerate_quantisation_blocks(dev, pv):
+    """Blocks whose quantisation scale is zero.  Head 0: an all-zero 64-token
+    Q block (sq = 0, so those queries see equal scores); head 1: every key the
+    same (K - kmean = 0, every sk = 0, so every query sees equal scores); head
+    2: an all-zero V channel (its FP8 scale is 0).  Outputs against the
+    emulation; the equal-score rows take the plain average of V, so they are
+    identical, and the zero channel is exactly zero."""
+    N, dt = 300, "bf16"
+    w = Workload(99, "int8-degenerate", dt, 1, 3, N, 128, k_offset_var=2.0)
+    inp = dict(make_inputs(w))
+    q, k, v = (inp[n].clone() for n in ("q", "k", "v"))
+    q[0, 0, 64:128] = 0
+    k[0, 1] = k[0, 1, :1].expand(N, -1)
+    v[0, 2, :, 5] = 0
+    inp.update(q=q, k=k, v=v)
+    say(f"case degenerate blocks pv={pv}")
+    o, lse = run(dev, inp, pv=pv)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    ref, ref_lse = sage.emulate(qn, kn, vn, w.scale, fa.fa_int8qk_kv_block(), return_lse=True,
+                                pv="fp8" if pv == "fp8" else EMU_PV[dt])
+    got = o.cpu().double().numpy()
+    err = np.abs(got - ref)
+    say(f"  max|err|={err.max():.3e} mean|err|={err.mean():.3e}")
+    assert np.all(err <= 1e-2 + HALF_ULP[w.torch_dtype] * np.abs(ref))
+    check_vs_emulation(got, ref, w.torch_dtype, f"degenerate pv={pv}")
+    oc = o.cpu()
+    assert torch.equal(oc[0, 0, 64:128], oc[0, 0, 64:65].expand(64, -1)), "zero Q block: equal rows"
+    assert torch.equal(oc[0, 1], oc[0, 1, :1].expand(N, -1)), "equal keys: equal rows"
+    assert torch.all(oc[0, 2, :, 5] == 0), "zero V channel"
+    lg = lse.cpu().double().numpy()
+    assert np.abs(lg - ref_lse).max() < 1e-4
+    assert np.allclose(lg[0, 1], math.log(N), atol=1e-5), "equal scores: lse = ln N"
+
+
 def test_int8qk_fully_masked_batch(dev):
     w = Workload(96, "int8-mask", "bf16", 2, 2, 100, 128)
     inp = make_inputs(w)

@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -40,13 +41,21 @@ CSRC = os.path.join(ROOT, "attention_fa_fwd_04_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank runs: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(" ".join(l.split()) for l in text.splitlines() if l.strip())
+
+
 def source_hash() -> str:
-    """Hash of the kernel sources: HBM-traffic counters taken from an older
-    build are not reported against a newer one."""
+    """Hash of the kernel sources' code (comments ignored): HBM-traffic
+    counters taken from an older build are not reported against a newer
+    one."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

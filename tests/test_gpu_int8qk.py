@@ -179,6 +179,39 @@ def test_int8qk_parity_small(dev, dt, keylen):
 
 
 @pytest.mark.parametrize("pv", ["fp8", "16"])
+def test_int8qk_deterministic_and_in_bounds(dev, pv):
+    """Through the C ABI: bitwise identical reruns (the phase-alternating
+    loops read LDS tiles that other waves' DMA fills, so a missing wait would
+    show as run-to-run differences) and guard bands around o and lse left
+    untouched; N = 1111 leaves a ragged last tile and a partial query block."""
+    w = Workload(97, f"int8-det-{pv}", "bf16", 1, 3, 1111, 128, k_offset_var=2.0)
+    inp = make_inputs(w)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    B, H, N, D = q.shape
+    G = 4096
+    guard = torch.full((G + q.numel() + G,), 7.0, dtype=q.dtype, device=dev)
+    lguard = torch.full((G + B * H * N + G,), 7.0, dtype=torch.float32, device=dev)
+    o = guard[G:G + q.numel()].view(q.shape)
+    lse = lguard[G:G + B * H * N].view(B, H, N)
+    size, entry = ((fa.fa_fwd_int8qk_workspace_bytes, fa.fa_fwd_int8qk) if pv == "fp8" else
+                   (fa.fa_fwd_int8qk_pv16_workspace_bytes, fa.fa_fwd_int8qk_pv16))
+    ws = torch.empty(size(B, H, N, D), dtype=torch.uint8, device=dev)
+    outs = []
+    for _ in range(3):
+        rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), None, B, H, N, D,
+                   w.scale, fa.FA_BF16, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        outs.append((o.clone(), lse.clone()))
+    for oo, ll in outs[1:]:
+        assert torch.equal(oo.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(ll.view(torch.int32), outs[0][1].view(torch.int32))
+    assert torch.all(guard[:G] == 7) and torch.all(guard[-G:] == 7)
+    assert torch.all(lguard[:G] == 7) and torch.all(lguard[-G:] == 7)
+    assert torch.isfinite(o).all()
+
+
+@pytest.mark.parametrize("pv", ["fp8", "16"])
 def test_degenerate_quantisation_blocks(dev, pv):
     """Blocks whose quantisation scale is zero.  Head 0: an all-zero 64-token
     Q block (sq = 0, so those queries see equal scores); head 1: every key the

@@ -114,6 +114,68 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The two-group phase schedule over nt full key tiles, shared by the D = 128
+// phase-alternating kernels (the schedule and buffer lifetimes are those of
+// the header above).  Tile t lives in K buffer t & 1 and V buffer t & 1.
+//   mma(tk, tv, pv, qk, pre)  MFMA phase on K tile tk and V tile tv; the
+//                             BoolTag flags select P V of the previous tile,
+//                             Q K^T of tile tk, and V operands of the first
+//                             P V step already read
+//   softmax(t)                softmax phase of tile t
+//   load_k(t), load_v(t)      this wave's share of tile t's DMA (group A
+//                             loads K tiles, group B V tiles)
+//   vread_first(t)            the first P V step's V operands of tile t
+// K(0) must be resident on entry; every wave passes 2 nt + 2 barriers.
+template <typename Mma, typename Soft, typename LoadK, typename LoadV, typename VFirst>
+__device__ __forceinline__ void pp_phase_loop(int grp, int nt, Mma&& mma, Soft&& softmax, LoadK&& load_k,
+                                              LoadV&& load_v, VFirst&& vread_first) {
+  if (grp == 0) {
+    mma(0, 0, BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
+    lds_barrier();                                            // phase 0
+    for (int t = 0; t + 1 < nt; ++t) {
+      // phase 2t + 1: K(t + 1), first read in phase 2t + 2, replaces K(t - 1),
+      // last read in phase 2t - 1
+      load_k(t + 1);
+      softmax(t);
+      __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
+      vread_first(t);                                         // V(t): landed by the end of phase 2t
+      lds_barrier();                                          // phase 2t + 1
+      mma(t + 1, t, BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
+      lds_barrier();                                          // phase 2t + 2
+    }
+    softmax(nt - 1);
+    vread_first(nt - 1);
+    lds_barrier();                                            // phase 2nt - 1
+    mma(0, nt - 1, BoolTag<true>{}, BoolTag<false>{}, BoolTag<true>{});
+    lds_barrier();                                            // phase 2nt
+    lds_barrier();                                            // phase 2nt + 1
+  } else {
+    load_v(0);                                                // V(0), buffer unused yet
+    // V(0) must be resident by the end of phase 0: group A reads it at the
+    // end of its first softmax phase, phase 1
+    __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): V(0) landed
+    lds_barrier();                                            // phase 0
+    mma(0, 0, BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
+    lds_barrier();                                            // phase 1
+    for (int t = 0; t + 1 < nt; ++t) {
+      // phase 2t + 2: V(t + 1), first read at the end of phase 2t + 3,
+      // replaces V(t - 1), last read in phase 2t + 1
+      load_v(t + 1);
+      softmax(t);
+      __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): V(t + 1) landed
+      vread_first(t);
+      lds_barrier();                                          // phase 2t + 2
+      mma(t + 1, t, BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
+      lds_barrier();                                          // phase 2t + 3
+    }
+    softmax(nt - 1);
+    vread_first(nt - 1);
+    lds_barrier();                                            // phase 2nt
+    mma(0, nt - 1, BoolTag<true>{}, BoolTag<false>{}, BoolTag<true>{});
+    lds_barrier();                                            // phase 2nt + 1
+  }
+}
+
 template <typename T, int BC, int MASK, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -431,51 +493,12 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pp_kernel(
       for (int i = 0; i < KB_B; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (kb4 + i) * 1024), 16, o[i] + row_off, 0, 0, 0);
     };
-    if (grp == 0) {
-      mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
-      lds_barrier();                                            // phase 0
-      for (int t = 0; t + 1 < nt; ++t) {
-        // phase 2t + 1: K(t + 1), first read in phase 2t + 2, replaces K(t - 1),
-        // last read in phase 2t - 1
-        dma4(kr, kbuf(t + 1), t + 1, ks, offs);
-        softmax_phase(t, BoolTag<false>{});
-        __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
-        vread_first(vbuf(t));                                   // V(t): landed by phase 2t (V(0): phase 0)
-        lds_barrier();                                          // phase 2t + 1
-        mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
-        lds_barrier();                                          // phase 2t + 2
-      }
-      softmax_phase(nt - 1, BoolTag<false>{});
-      vread_first(vbuf(nt - 1));
-      lds_barrier();                                            // phase 2nt - 1
-      mma_phase(kbuf(0), vbuf(nt - 1), BoolTag<true>{}, BoolTag<false>{}, BoolTag<true>{});
-      lds_barrier();                                            // phase 2nt
-      lds_barrier();                                            // phase 2nt + 1
-    } else {
-      dma4(vr, vbuf(0), 0, vs, offs);                           // V(0), buffer unused yet
-      // V(0) must be resident by the end of phase 0: group A pre-reads it
-      // at the end of its first softmax phase, phase 1
-      __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0): V(0) landed
-      lds_barrier();                                            // phase 0
-      mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
-      lds_barrier();                                            // phase 1
-      for (int t = 0; t + 1 < nt; ++t) {
-        // phase 2t + 2: V(t + 1), first read at the end of phase 2t + 3,
-        // replaces V(t - 1), last read in phase 2t + 1
-        dma4(vr, vbuf(t + 1), t + 1, vs, offs);
-        softmax_phase(t, BoolTag<false>{});
-        __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): V(t + 1) landed
-        vread_first(vbuf(t));
-        lds_barrier();                                          // phase 2t + 2
-        mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
-        lds_barrier();                                          // phase 2t + 3
-      }
-      softmax_phase(nt - 1, BoolTag<false>{});
-      vread_first(vbuf(nt - 1));
-      lds_barrier();                                            // phase 2nt
-      mma_phase(kbuf(0), vbuf(nt - 1), BoolTag<true>{}, BoolTag<false>{}, BoolTag<true>{});
-      lds_barrier();                                            // phase 2nt + 1
-    }
+    pp_phase_loop(
+        grp, nt,
+        [&](int tk, int tv, auto pv, auto qk, auto pre) { mma_phase(kbuf(tk), vbuf(tv), pv, qk, pre); },
+        [&](int t) { softmax_phase(t, BoolTag<false>{}); },
+        [&](int t) { dma4(kr, kbuf(t), t, ks, offs); }, [&](int t) { dma4(vr, vbuf(t), t, vs, offs); },
+        [&](int t) { vread_first(vbuf(t)); });
   }
 
   float l_tot = wave_sum_halves(l_run);

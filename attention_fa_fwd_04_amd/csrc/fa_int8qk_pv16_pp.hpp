@@ -32,9 +32,10 @@
 // Group A loads K(t+1) at the start of its
 // softmax phase 2t + 1 (two 1 KB instructions per wave), group B loads
 // V(t+1) at the start of its softmax phase 2t + 2 (four per wave); each
-// waits for its own DMA before the phase's closing barrier, and buffer
-// lifetimes are those of fa_fwd_pp_kernel.  Each group reads the first
-// P V step's V operands at the end of its softmax phase.
+// waits for its own DMA before the phase's closing barrier; the schedule
+// is fa_fwd_pp.hpp's pp_phase_loop, with the buffer lifetimes of
+// fa_fwd_pp_kernel.  Each group reads the first P V step's V operands at the
+// end of its softmax phase.
 #pragma once
 
 #include "fa_int8qk.hpp"
@@ -278,51 +279,11 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(buf + (4 * w4 + i) * 1024), 16, offs[i] + row_off, 0,
                                                  0, 0);
     };
-    if (grp == 0) {
-      mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
-      lds_barrier();                                            // phase 0
-      for (int t = 0; t + 1 < nt; ++t) {
-        // phase 2t + 1: K(t + 1), first read in phase 2t + 2, replaces K(t - 1),
-        // last read in phase 2t - 1
-        dma_k(kbuf(t + 1), t + 1);
-        softmax_phase(t, BoolTag<false>{});
-        __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
-        vread_first(vbuf(t));                                   // V(t): landed by the end of phase 2t
-        lds_barrier();                                          // phase 2t + 1
-        mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
-        lds_barrier();                                          // phase 2t + 2
-      }
-      softmax_phase(nt - 1, BoolTag<false>{});
-      vread_first(vbuf(nt - 1));
-      lds_barrier();                                            // phase 2nt - 1
-      mma_phase(kbuf(0), vbuf(nt - 1), BoolTag<true>{}, BoolTag<false>{}, BoolTag<true>{});
-      lds_barrier();                                            // phase 2nt
-      lds_barrier();                                            // phase 2nt + 1
-    } else {
-      dma_v(vbuf(0), 0);                                        // V(0), buffer unused yet
-      // V(0) must be resident by the end of phase 0: group A reads it at
-      // the end of its first softmax phase, phase 1
-      __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
-      lds_barrier();                                            // phase 0
-      mma_phase(kbuf(0), vbuf(0), BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
-      lds_barrier();                                            // phase 1
-      for (int t = 0; t + 1 < nt; ++t) {
-        // phase 2t + 2: V(t + 1), first read at the end of phase 2t + 3,
-        // replaces V(t - 1), last read in phase 2t + 1
-        dma_v(vbuf(t + 1), t + 1);
-        softmax_phase(t, BoolTag<false>{});
-        __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0): V(t + 1) landed
-        vread_first(vbuf(t));
-        lds_barrier();                                          // phase 2t + 2
-        mma_phase(kbuf(t + 1), vbuf(t), BoolTag<true>{}, BoolTag<true>{}, BoolTag<true>{});
-        lds_barrier();                                          // phase 2t + 3
-      }
-      softmax_phase(nt - 1, BoolTag<false>{});
-      vread_first(vbuf(nt - 1));
-      lds_barrier();                                            // phase 2nt
-      mma_phase(kbuf(0), vbuf(nt - 1), BoolTag<true>{}, BoolTag<false>{}, BoolTag<true>{});
-      lds_barrier();                                            // phase 2nt + 1
-    }
+    pp_phase_loop(
+        grp, nt,
+        [&](int tk, int tv, auto pv, auto qk, auto pre) { mma_phase(kbuf(tk), vbuf(tv), pv, qk, pre); },
+        [&](int t) { softmax_phase(t, BoolTag<false>{}); }, [&](int t) { dma_k(kbuf(t), t); },
+        [&](int t) { dma_v(vbuf(t), t); }, [&](int t) { vread_first(vbuf(t)); });
   }
   // The ragged last tile, all eight waves in step, after every full tile
   // (both groups have passed barrier 2nt + 1, so every buffer is free).

@@ -10,8 +10,10 @@
 // in key order, the ragged last tile last, so every P is rounded against the
 // same running max as there; only the fp32 accumulation order inside P V
 // differs.
-// No additive mask and no Q smoothing (those take fa_int8qk_pv16_kernel); a
-// key-length mask shortens the key range.
+// A key-length mask shortens the key range; an additive mask is added to
+// every scaled score (scale, then the mask times log2(e), as in the in-step
+// kernel), its values for a tile loaded while the tile's Q K^T runs.  Q
+// smoothing takes fa_int8qk_pv16_kernel.
 //
 // Schedule.  8 waves of 32 query rows, one workgroup per CU; waves w and
 // w + 4 share a SIMD, so waves 0-3 (group A) and 4-7 (group B) hold one wave
@@ -53,7 +55,6 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
   constexpr int VROW = 2 * BC;                  // 16-bit V^T row (64 keys), 128 bytes
   constexpr int VBYTES = D * VROW;
   static_assert(KBYTES == 8192 && VBYTES == 16384, "8 and 16 DMA instructions per tile");
-  static_assert(MASK != kMaskAdd, "additive masks take fa_int8qk_pv16_kernel");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KBYTES + 2 * VBYTES];   // K0 K1 V0 V1
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
   const int ln = lane & 31, lh = lane >> 5;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt, qt = logical - bh * nqt;
-  const int b = bh / H;
+  const int b = bh / H, h = bh - b * H;
 
   int n_eff = N;
   if constexpr (MASK == kMaskLen) {
@@ -87,6 +88,16 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
   // every query of a wave lies in one 64-token scale block
   const float sq_w = sq[(size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)];
   const float* skh = sk + (size_t)bh * groups;
+  // additive mask: this lane's query row (row 0 stands in for rows past N,
+  // whose results are not stored); mk holds the current tile's values
+  constexpr bool kAdd = MASK == kMaskAdd;
+  const float* mrow = nullptr;
+  bool mvec = false;
+  if constexpr (kAdd) {
+    mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh + (int64_t)(q_ok ? q_row : 0) * mask.sq;
+    mvec = mask_rows_vec4(mask);
+  }
+  float mk[32];
 
   // DMA offsets (tile 0) of 1 KB block kb: rows 8 kb + lane / 8 (of K, or
   // of V^T), chunk lane % 8 fetching logical chunk (lane % 8) ^ ((r / 2) % 8).
@@ -204,7 +215,10 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
+          if constexpr (kAdd)                     // keys past N read -inf
+            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i] * kLog2e);
+          else
+            s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
         }
       mx = -INFINITY;
 #pragma unroll
@@ -281,8 +295,11 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
     };
     pp_phase_loop(
         grp, nt,
-        [&](int tk, int tv, auto pv, auto qk, auto pre) { mma_phase(kbuf(tk), vbuf(tv), pv, qk, pre); },
-        [&](int t) { softmax_phase(t, BoolTag<false>{}); }, [&](int t) { dma_k(kbuf(t), t); },
+        [&](int tk, int tv, auto pv, auto qk, auto pre) {
+          if constexpr (kAdd && decltype(qk)::value) load_mask_tile<2>(mk, mrow, mask.sk, mvec, tk * BC, n_eff, lh);
+          mma_phase(kbuf(tk), vbuf(tv), pv, qk, pre);
+        },
+        [&](int t) { softmax_phase(t, BoolTag<kAdd>{}); }, [&](int t) { dma_k(kbuf(t), t); },
         [&](int t) { dma_v(vbuf(t), t); }, [&](int t) { vread_first(vbuf(t)); });
   }
   // The ragged last tile, all eight waves in step, after every full tile
@@ -292,6 +309,7 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
     dma_v_all(nt, vbuf0);
     __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
     __syncthreads();
+    if constexpr (kAdd) load_mask_tile<2>(mk, mrow, mask.sk, mvec, nt * BC, n_eff, lh);
     mma_phase(kbuf0, vbuf0, BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
     softmax_phase(nt, BoolTag<true>{});
     mma_phase(kbuf0, vbuf0, BoolTag<true>{}, BoolTag<false>{}, BoolTag<false>{});
@@ -314,20 +332,22 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
   }
 }
 
-// The 16-bit-PV form: the phase-alternating kernel for full runs of key
-// tiles without a per-key term (no mask or a key length);
-// fa_int8qk_pv16_kernel takes additive masks and Q smoothing.
+// The 16-bit-PV form: the phase-alternating kernel for every mask;
+// fa_int8qk_pv16_kernel takes Q smoothing.
 template <typename T>
 int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse, int mask_kind, MaskArgs m,
                        int B, int H, int N, float scale, void* workspace, const Int8Layout& L, bool smooth,
                        hipStream_t st) {
   const Int8Ops op = int8_prepass<T, true>(q, k, v, B, H, N, scale, workspace, L, smooth, st);
-  if (!smooth && mask_kind != kMaskAdd) {
+  if (!smooth) {
     const int nqt = (N + 255) / 256;
     const dim3 grid(B * H * nqt), block(512);
     const T* V = static_cast<const T*>(op.vt);
     if (mask_kind == kMaskLen)
       hipLaunchKernelGGL((fa_int8qk_pv16_pp_kernel<T, kMaskLen>), grid, block, 0, st, op.q8, op.k8, V, op.sq, op.sk,
+                         m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
+    else if (mask_kind == kMaskAdd)
+      hipLaunchKernelGGL((fa_int8qk_pv16_pp_kernel<T, kMaskAdd>), grid, block, 0, st, op.q8, op.k8, V, op.sq, op.sk,
                          m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
     else
       hipLaunchKernelGGL((fa_int8qk_pv16_pp_kernel<T, kMaskNone>), grid, block, 0, st, op.q8, op.k8, V, op.sq, op.sk,
@@ -340,12 +360,8 @@ int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, flo
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, op.q8, op.k8, static_cast<const T*>(op.vt), op.sq, op.sk,
                        op.comp, m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
   };
-  if (smooth) {
-    if (mask_kind == kMaskLen) go(fa_int8qk_pv16_kernel<T, kMaskLen, true>);
-    else go(fa_int8qk_pv16_kernel<T, kMaskNone, true>);
-  } else {
-    go(fa_int8qk_pv16_kernel<T, kMaskAdd, false>);
-  }
+  if (mask_kind == kMaskLen) go(fa_int8qk_pv16_kernel<T, kMaskLen, true>);
+  else go(fa_int8qk_pv16_kernel<T, kMaskNone, true>);
   return FA_OK;
 }
 

@@ -704,231 +704,6 @@ __global__ __launch_bounds__(256, 2) void fa_int8qk_kernel(
   }
 }
 
-// INT8-QK / 16-bit-PV form: the same Q K^T and online softmax as
-// fa_int8qk_kernel, with P rounded to the input's 16-bit type (P <= 1 against
-// the running max) and V^T read unquantised from the workspace (keys permuted
-// per 32 by v16_pos); P V runs on the 16-bit 32x32x16 MFMA, four per 32
-// channels per 64-key tile.  Launched for additive masks and Q smoothing;
-// other calls take the phase-alternating fa_int8qk_pv16_pp_kernel (same V^T).
-template <typename T, int MASK, bool SQ>
-__global__ __launch_bounds__(256, 2) void fa_int8qk_pv16_kernel(
-    const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const T* __restrict__ vt,
-    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ comp,
-    MaskArgs mask, T* __restrict__ O, float* __restrict__ LSE,
-    int H, int N, int npad, int groups, int nqt, float c_log2) {
-  constexpr int D = 128, BC = kInt8Bc, BR = 128, NT = 256;
-  constexpr int KSTR = D + 16;                  // int8 K row + pad
-  constexpr int VSTR = 2 * BC + 16;             // 16-bit V^T row (64 keys) + pad
-  constexpr int KBYTES = BC * KSTR, VBYTES = D * VSTR, BUF = KBYTES + VBYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ln = lane & 31, lh = lane >> 5;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nqt, qt = logical - bh * nqt;
-  const int b = bh / H, h = bh - b * H;
-
-  int n_eff = N;
-  if constexpr (MASK == kMaskLen) {
-    const int L = reinterpret_cast<const int*>(mask.ptr)[b];
-    n_eff = L < 0 ? 0 : (L > N ? N : L);
-  }
-  const int ntiles = (n_eff + BC - 1) / BC;
-
-  const int8_t* Qh = q8 + (size_t)bh * npad * D;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(k8 + (size_t)bh * npad * D, (uint32_t)npad * D);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vt + (size_t)bh * D * npad, (uint32_t)D * npad * 2);
-
-  const int q_row = qt * BR + wave * 32 + ln;
-  const bool q_ok = q_row < N;
-  // rows past N are zero codes in the workspace (npad >= q_row + 1 within the tile)
-  u32x4 qreg[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    qreg[s] = *reinterpret_cast<const u32x4*>(Qh + (size_t)min(q_row, npad - 1) * D + (2 * s + lh) * 16);
-  // every query of a wave lies in one 64-token scale block
-  const float sq_w = sq[(size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)];
-  const float* skh = sk + (size_t)bh * groups;
-  // additive mask: this lane's query row (row 0 stands in for rows past N,
-  // whose results are not stored)
-  const float* mrow = nullptr;
-  bool mvec = false;
-  if constexpr (MASK == kMaskAdd) {
-    mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh + (int64_t)(q_ok ? q_row : 0) * mask.sq;
-    mvec = mask_rows_vec4(mask);
-  }
-  static_assert(!(SQ && MASK == kMaskAdd), "Q smoothing takes no additive mask");
-  if constexpr (SQ) {   // the compensation row of the wave's query block (rows are npad floats, aligned)
-    mrow = comp + ((size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)) * npad;
-    mvec = true;
-  }
-  constexpr bool kRowTerm = SQ || MASK == kMaskAdd;   // a per-key term on every tile
-
-  // staging: K tile 64 rows x 8 chunks (2 per thread), V^T tile 128 rows x 8
-  // chunks (4 per thread)
-  u32x4 kst[2], vst[4];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) kst[i] = buf_load16(kr, (uint32_t)(j * BC) * D + (tid + NT * i) * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int it = tid + NT * i;
-      const int d = it >> 3, c = it & 7;
-      vst[i] = buf_load16(vr, ((uint32_t)d * npad + j * BC) * 2 + c * 16);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint8_t* kb = smem + buf * BUF;
-    uint8_t* vb = kb + KBYTES;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int it = tid + NT * i;
-      *reinterpret_cast<u32x4*>(kb + (it >> 3) * KSTR + (it & 7) * 16) = kst[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int it = tid + NT * i;
-      *reinterpret_cast<u32x4*>(vb + (it >> 3) * VSTR + (it & 7) * 16) = vst[i];
-    }
-  };
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 acc[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[p][i] = 0.f;
-
-  auto step = [&](int j, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const int buf = j & 1;
-    // additive mask values of this lane's 32 keys (keys past N read -inf),
-    // issued before the next tile's loads so that waiting for them does not
-    // wait for those too (loads complete in issue order)
-    float mk[32];
-    if constexpr (kRowTerm) load_mask_tile<2>(mk, mrow, SQ ? 1 : mask.sk, mvec, j * BC, n_eff, lh);
-    load_tile(j + 1);
-    const uint8_t* kb = smem + buf * BUF;
-    const uint8_t* vb = kb + KBYTES;
-    const int kv0 = j * BC;
-    const float c = sq_w * skh[j] * c_log2;       // one K scale block per tile
-
-    i32x16 si[2];
-#pragma unroll
-    for (int G = 0; G < 2; ++G) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) si[G][i] = kAccBias;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (32 * G + ln) * KSTR + (2 * st + lh) * 16);
-        si[G] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
-                                                      __builtin_bit_cast(i32x4, qreg[st]), si[G], 0, 0, 0);
-      }
-    }
-    // Full tiles: the row max is taken on the exact int32 sums and scaled once
-    // (the tile's scale c is >= 0), and the scale is folded into the exp2 FMA.
-    // The ragged last tile, and every tile under an additive mask, scales
-    // first (then adds the mask) so dropped keys can be -inf.
-    float s[32];
-    float mx;
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if constexpr (SQ)                           // table already in log2 units; -inf past n_eff
-            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i]);
-          else if constexpr (MASK == kMaskAdd)
-            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i] * kLog2e);
-          else
-            s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
-        }
-      mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) mx = fmaxf(mx, s[i]);
-    } else {
-      // the max of the exact integer-valued floats (measured faster here than
-      // the integer max, which the FP8 kernel keeps)
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[16 * G + i] = unbias(si[G][i]);
-      float fmx = s[0];
-#pragma unroll
-      for (int i = 1; i < 32; ++i) fmx = fmaxf(fmx, s[i]);
-      mx = fmx * c;
-    }
-    mx = wave_max_halves_valu(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
-      l_run *= alpha;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[p][i] *= alpha;
-    }
-    // P = exp2(s - m) <= 1, rounded to the 16-bit type for the P V operand
-    auto pexp = [&](float x) {
-      return MASKED ? __builtin_amdgcn_exp2f(x - m_use) : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -m_use));
-    };
-    float psum = -0.f;                            // -0 + x == x: the first add folds away
-    float pv[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      pv[i] = pexp(s[i]);
-      psum += pv[i];
-    }
-    l_run += psum;
-    // P^T operand for (key block G, 8-key half cc): the lane's scores
-    // 16 G + 8 cc .. +7, keys 32 G + 16 cc + {0..3, 8..11} + 4 lh; the V^T
-    // operand holds the same keys at positions 16 lh + 8 cc .. +7 of block G.
-#pragma unroll
-    for (int G = 0; G < 2; ++G)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const u32x4 bop = pack_chunk<T>(pv + 16 * G + 8 * cc);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const u32x4 aop = *reinterpret_cast<const u32x4*>(vb + (32 * p + ln) * VSTR + (32 * G + 16 * lh + 8 * cc) * 2);
-          acc[p] = mfma_chunk<T>(aop, bop, acc[p]);
-        }
-      }
-    store_tile(buf ^ 1);
-    __syncthreads();
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  if constexpr (kRowTerm) {
-    for (int j = 0; j < ntiles; ++j) step(j, BoolTag<true>{});
-  } else {
-    const int nfull = n_eff / BC;
-    for (int j = 0; j < nfull; ++j) step(j, BoolTag<false>{});
-    if (nfull < ntiles) step(nfull, BoolTag<true>{});
-  }
-
-  const float l_tot = wave_sum_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_ok) {
-    T* orow = O + ((size_t)bh * N + q_row) * D;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * p + 8 * g + 4 * lh;
-        store4<T>(orow + d0, acc[p][4 * g] * inv, acc[p][4 * g + 1] * inv,
-                  acc[p][4 * g + 2] * inv, acc[p][4 * g + 3] * inv);
-      }
-    if (LSE != nullptr && lh == 0)
-      LSE[(size_t)bh * N + q_row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  }
-}
-
 // Prepass launches (statistics, quantisation, and with Q smoothing the
 // compensation table) shared by both P V forms; returns the operands.
 struct Int8Ops {

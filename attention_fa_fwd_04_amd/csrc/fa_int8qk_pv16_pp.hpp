@@ -3,17 +3,17 @@
 // section "SageAttention": INT8 Q K^T on integer matrix cores, P V with
 // 16-bit operands).
 //
-// Arithmetic of fa_int8qk_pv16_kernel: exact int32 scores S = Q8 K8^T,
-// scaled by sq * sk * scale log2(e); exact running row max per 64-key tile
-// (P <= 1 against it, no lazy rescale); P rounded to the input's 16-bit type
-// for the P V MFMA; l sums the unrounded P; O = acc / l.  Tiles are visited
-// in key order, the ragged last tile last, so every P is rounded against the
-// same running max as there; only the fp32 accumulation order inside P V
-// differs.
-// A key-length mask shortens the key range; an additive mask is added to
-// every scaled score (scale, then the mask times log2(e), as in the in-step
-// kernel), its values for a tile loaded while the tile's Q K^T runs.  Q
-// smoothing takes fa_int8qk_pv16_kernel.
+// Arithmetic: exact int32 scores S = Q8 K8^T, scaled by sq * sk * scale
+// log2(e); exact running row max per 64-key tile (P <= 1 against it, no lazy
+// rescale); P rounded to the input's 16-bit type for the P V MFMA; l sums the
+// unrounded P; O = acc / l.  Tiles are visited in key order, the ragged last
+// tile last, so every P is rounded against the running max of the tiles up
+// to its own, the order the emulation fixes.
+// A key-length mask shortens the key range.  A per-key row term is added to
+// every scaled score, its values for a tile loaded while the tile's Q K^T
+// runs: an additive mask times log2(e) (scale, then the mask), or with Q
+// smoothing (SQ) the compensation row of the wave's 64-token query block,
+// which the prepass tabulates in log2 units.
 //
 // Schedule.  8 waves of 32 query rows, one workgroup per CU; waves w and
 // w + 4 share a SIMD, so waves 0-3 (group A) and 4-7 (group B) hold one wave
@@ -45,11 +45,11 @@
 
 namespace fa {
 
-template <typename T, int MASK>
+template <typename T, int MASK, bool SQ>
 __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
     const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const T* __restrict__ vt,
-    const float* __restrict__ sq, const float* __restrict__ sk, MaskArgs mask, T* __restrict__ O,
-    float* __restrict__ LSE, int H, int N, int npad, int groups, int nqt, float c_log2) {
+    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ comp, MaskArgs mask,
+    T* __restrict__ O, float* __restrict__ LSE, int H, int N, int npad, int groups, int nqt, float c_log2) {
   constexpr int D = 128, BC = kInt8Bc, BR = 256;
   constexpr int KBYTES = BC * D;                // int8 K tile, 128-byte rows
   constexpr int VROW = 2 * BC;                  // 16-bit V^T row (64 keys), 128 bytes
@@ -88,14 +88,24 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
   // every query of a wave lies in one 64-token scale block
   const float sq_w = sq[(size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)];
   const float* skh = sk + (size_t)bh * groups;
-  // additive mask: this lane's query row (row 0 stands in for rows past N,
-  // whose results are not stored); mk holds the current tile's values
+  // The per-key row term: an additive mask's row for this lane's query (row
+  // 0 stands in for rows past N, whose results are not stored), or the
+  // compensation row of the wave's query block (rows of npad floats,
+  // 256-byte aligned); mk holds the current tile's values.
   constexpr bool kAdd = MASK == kMaskAdd;
+  constexpr bool kRowTerm = kAdd || SQ;
+  static_assert(!(SQ && kAdd), "Q smoothing takes no additive mask");
   const float* mrow = nullptr;
+  int64_t mstride = 1;
   bool mvec = false;
   if constexpr (kAdd) {
     mrow = reinterpret_cast<const float*>(mask.ptr) + b * mask.sb + h * mask.sh + (int64_t)(q_ok ? q_row : 0) * mask.sq;
+    mstride = mask.sk;
     mvec = mask_rows_vec4(mask);
+  }
+  if constexpr (SQ) {
+    mrow = comp + ((size_t)bh * groups + min((qt * BR + wave * 32) / kQBlock, groups - 1)) * npad;
+    mvec = true;
   }
   float mk[32];
 
@@ -215,7 +225,9 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * G + 8 * (i >> 2) + 4 * lh + (i & 3);
-          if constexpr (kAdd)                     // keys past N read -inf
+          if constexpr (SQ)                       // table in log2 units; -inf past n_eff
+            s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i]);
+          else if constexpr (kAdd)                // keys past N read -inf
             s[16 * G + i] = __builtin_fmaf(unbias(si[G][i]), c, mk[16 * G + i] * kLog2e);
           else
             s[16 * G + i] = key < n_eff ? unbias(si[G][i]) * c : -INFINITY;
@@ -296,10 +308,10 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
     pp_phase_loop(
         grp, nt,
         [&](int tk, int tv, auto pv, auto qk, auto pre) {
-          if constexpr (kAdd && decltype(qk)::value) load_mask_tile<2>(mk, mrow, mask.sk, mvec, tk * BC, n_eff, lh);
+          if constexpr (kRowTerm && decltype(qk)::value) load_mask_tile<2>(mk, mrow, mstride, mvec, tk * BC, n_eff, lh);
           mma_phase(kbuf(tk), vbuf(tv), pv, qk, pre);
         },
-        [&](int t) { softmax_phase(t, BoolTag<kAdd>{}); }, [&](int t) { dma_k(kbuf(t), t); },
+        [&](int t) { softmax_phase(t, BoolTag<kRowTerm>{}); }, [&](int t) { dma_k(kbuf(t), t); },
         [&](int t) { dma_v(vbuf(t), t); }, [&](int t) { vread_first(vbuf(t)); });
   }
   // The ragged last tile, all eight waves in step, after every full tile
@@ -309,7 +321,7 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
     dma_v_all(nt, vbuf0);
     __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0)
     __syncthreads();
-    if constexpr (kAdd) load_mask_tile<2>(mk, mrow, mask.sk, mvec, nt * BC, n_eff, lh);
+    if constexpr (kRowTerm) load_mask_tile<2>(mk, mrow, mstride, mvec, nt * BC, n_eff, lh);
     mma_phase(kbuf0, vbuf0, BoolTag<false>{}, BoolTag<true>{}, BoolTag<false>{});
     softmax_phase(nt, BoolTag<true>{});
     mma_phase(kbuf0, vbuf0, BoolTag<true>{}, BoolTag<false>{}, BoolTag<false>{});
@@ -332,36 +344,28 @@ __global__ __launch_bounds__(512, 1) void fa_int8qk_pv16_pp_kernel(
   }
 }
 
-// The 16-bit-PV form: the phase-alternating kernel for every mask;
-// fa_int8qk_pv16_kernel takes Q smoothing.
+// The 16-bit-PV form: every mask, with or without Q smoothing.
 template <typename T>
 int launch_int8qk_pv16(const void* q, const void* k, const void* v, void* o, float* lse, int mask_kind, MaskArgs m,
                        int B, int H, int N, float scale, void* workspace, const Int8Layout& L, bool smooth,
                        hipStream_t st) {
   const Int8Ops op = int8_prepass<T, true>(q, k, v, B, H, N, scale, workspace, L, smooth, st);
-  if (!smooth) {
-    const int nqt = (N + 255) / 256;
-    const dim3 grid(B * H * nqt), block(512);
-    const T* V = static_cast<const T*>(op.vt);
-    if (mask_kind == kMaskLen)
-      hipLaunchKernelGGL((fa_int8qk_pv16_pp_kernel<T, kMaskLen>), grid, block, 0, st, op.q8, op.k8, V, op.sq, op.sk,
-                         m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
-    else if (mask_kind == kMaskAdd)
-      hipLaunchKernelGGL((fa_int8qk_pv16_pp_kernel<T, kMaskAdd>), grid, block, 0, st, op.q8, op.k8, V, op.sq, op.sk,
-                         m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
-    else
-      hipLaunchKernelGGL((fa_int8qk_pv16_pp_kernel<T, kMaskNone>), grid, block, 0, st, op.q8, op.k8, V, op.sq, op.sk,
-                         m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
-    return FA_OK;
-  }
-  const int nqt = (N + 127) / 128;
-  const int grid = B * H * nqt;
+  const int nqt = (N + 255) / 256;
+  const T* vt = static_cast<const T*>(op.vt);
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, op.q8, op.k8, static_cast<const T*>(op.vt), op.sq, op.sk,
-                       op.comp, m, static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
+    hipLaunchKernelGGL(kernel, dim3(B * H * nqt), dim3(512), 0, st, op.q8, op.k8, vt, op.sq, op.sk, op.comp, m,
+                       static_cast<T*>(o), lse, H, N, L.npad, L.groups, nqt, scale * kLog2e);
   };
-  if (mask_kind == kMaskLen) go(fa_int8qk_pv16_kernel<T, kMaskLen, true>);
-  else go(fa_int8qk_pv16_kernel<T, kMaskNone, true>);
+  if (smooth) {   // additive masks are refused with Q smoothing (host check)
+    if (mask_kind == kMaskLen) go(fa_int8qk_pv16_pp_kernel<T, kMaskLen, true>);
+    else go(fa_int8qk_pv16_pp_kernel<T, kMaskNone, true>);
+  } else if (mask_kind == kMaskLen) {
+    go(fa_int8qk_pv16_pp_kernel<T, kMaskLen, false>);
+  } else if (mask_kind == kMaskAdd) {
+    go(fa_int8qk_pv16_pp_kernel<T, kMaskAdd, false>);
+  } else {
+    go(fa_int8qk_pv16_pp_kernel<T, kMaskNone, false>);
+  }
   return FA_OK;
 }
 
